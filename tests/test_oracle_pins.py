@@ -1,0 +1,408 @@
+"""Pins for the fp64 oracle: each check ties it to something fixed outside it.
+
+What pins what:
+
+* byte fixtures (tests/golden/canonical_codes.txt, hand-written) -> unpacking and the
+  synthetic generator's canonical packing;
+* hand-dequantised codes (tests/golden/hand_dequant_s0p01_z8.txt, worked out by hand)
+  -> the dequantisation rule and the fp16 -> fp64 conversion of s and z;
+* exact rational brute force on tiny inputs, with its own bit-string unpacking,
+  within the fp64 dot-product error bound -> the whole linear map;
+* integer special case s = 1 (any integer z), reducing to numpy int64 matmul -> operand
+  order and transposition;
+* closed forms (X = 0, q = z, a constant over one group) -> group indexing;
+* the channel-equalisation identity (ninfer-3080 performance notes, "cuBLAS prefill
+  route": a per-channel factor moved from the activations into the weights leaves the
+  product unchanged), here with power-of-two factors per group so that it is bit-exact;
+* k-permutation within a group (ninfer-3080 performance notes, "What changed",
+  "Permuted k order"), whole-group permutation, row permutation, token independence;
+* silu against scipy's logistic function and textbook values; LinearAdd special cases.
+
+``test_planted_mistakes_are_caught`` plants plausible mistakes in the oracle and
+checks that at least one pin fails for each.
+"""
+from __future__ import annotations
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from oracle import reference as ref
+from synth import pack_canonical
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+
+def _tiny_case(rng, N, K, T, bits, zero_mode="int"):
+    q = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+    # make sure every code value appears when there is room for it
+    flat = q.reshape(-1)
+    nvals = min(flat.size, 1 << bits)
+    flat[:nvals] = np.arange(nvals, dtype=np.uint8)
+    G = K // 64
+    s = rng.uniform(0.005, 0.02, size=(N, G)).astype(np.float16)
+    if zero_mode == "int":
+        z = rng.integers(0, 1 << bits, size=(N, G)).astype(np.float16)
+    else:
+        z = rng.uniform(0, 1 << bits, size=(N, G)).astype(np.float16)
+    x = rng.standard_normal((T, K)).astype(np.float16)
+    lo, hi = pack_canonical(q, bits)
+    return q, lo, hi, s, z, x
+
+
+def _bitstring_codes(lo_row, hi_row, K, bits):
+    """Independent unpacking: read each code's bits off the bytes' binary strings."""
+    codes = []
+    for k in range(K):
+        b = format(int(lo_row[k // 2]), "08b")      # MSB first
+        nib = b[4:] if k % 2 == 0 else b[:4]
+        v = int(nib, 2)
+        if bits == 5:
+            hb = format(int(hi_row[k // 8]), "08b")[7 - (k % 8)]
+            v += 16 * int(hb)
+        codes.append(v)
+    return codes
+
+
+def _read_code_fixtures():
+    rows = []
+    with open(os.path.join(GOLDEN, "canonical_codes.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            head, lo_s, hi_s, codes_s = [p.strip() for p in line.split("|")]
+            bits, K = (int(v) for v in head.split())
+            lo = np.array([int(h, 16) for h in lo_s.split()], dtype=np.uint8)[None, :]
+            hi = None if hi_s == "-" else np.array([int(h, 16) for h in hi_s.split()],
+                                                   dtype=np.uint8)[None, :]
+            codes = np.array([int(c) for c in codes_s.split()], dtype=np.int64)
+            rows.append((bits, K, lo, hi, codes))
+    return rows
+
+
+# ---------------------------------------------------------------- pin checks
+# Each check_* raises AssertionError on a mismatch.  They look the oracle's
+# functions up at call time so that the planted-mistake test can patch them.
+
+def check_unpack_fixtures():
+    for bits, K, lo, hi, codes in _read_code_fixtures():
+        got = ref.unpack_codes(lo, hi, K, bits)[0]
+        assert np.array_equal(got, codes), (bits, K, got, codes)
+
+
+def check_hand_dequant():
+    s16 = np.float16(0.01)
+    assert s16.view(np.uint16) == 0x211F
+    assert Fraction(float(s16)) == Fraction(1311, 131072)
+    table = {}
+    with open(os.path.join(GOLDEN, "hand_dequant_s0p01_z8.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            qv, num, _dec = line.split()
+            table[int(qv)] = Fraction(int(num), 131072)
+    # one row holding every code once in a 64-column group
+    q = np.zeros((1, 64), dtype=np.int64)
+    q[0, :16] = np.arange(16)
+    s = np.full((1, 1), 0.01, dtype=np.float16)
+    z = np.full((1, 1), 8, dtype=np.float16)
+    w = ref.dequantize(q, s, z)
+    for qv in range(16):
+        assert Fraction(float(w[0, qv])) == table[qv], (qv, w[0, qv])
+    # and through the full linear map with one-hot activations
+    lo, _ = pack_canonical(q.astype(np.uint8), 4)
+    for qv in (0, 7, 8, 15):
+        x = np.zeros((1, 64), dtype=np.float16)
+        x[0, qv] = 1.0
+        y = ref.linear(x, lo, None, s, z, 4)
+        assert Fraction(float(y[0, 0])) == table[qv]
+
+
+def check_bruteforce_exact():
+    rng = np.random.default_rng(1234)
+    for bits in (4, 5):
+        for (N, K, T) in ((1, 64, 1), (3, 64, 2), (4, 128, 3), (2, 128, 1)):
+            for zero_mode in ("int", "real"):
+                q, lo, hi, s, z, x = _tiny_case(rng, N, K, T, bits, zero_mode)
+                y = ref.linear(x, lo, hi, s, z, bits)
+                assert y.shape == (T, N)
+                eps = 2.0 ** -53
+                for n in range(N):
+                    codes = _bitstring_codes(lo[n], None if hi is None else hi[n], K, bits)
+                    for t in range(T):
+                        exact = Fraction(0)
+                        mag = Fraction(0)
+                        for k in range(K):
+                            g = k // 64
+                            w = Fraction(float(s[n, g])) * (codes[k] - Fraction(float(z[n, g])))
+                            term = Fraction(float(x[t, k])) * w
+                            exact += term
+                            mag += abs(term)
+                        bound = (K + 4) * eps * mag
+                        err = abs(Fraction(float(y[t, n])) - exact)
+                        assert err <= bound, (bits, N, K, T, n, t, float(err), float(bound))
+
+
+def check_integer_special_case():
+    rng = np.random.default_rng(7)
+    for bits in (4, 5):
+        N, K, T = 24, 192, 5
+        q = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+        lo, hi = pack_canonical(q, bits)
+        z_int = rng.integers(0, 1 << bits, size=(N, K // 64))
+        s = np.ones((N, K // 64), dtype=np.float16)
+        z = z_int.astype(np.float16)
+        xi = rng.integers(-8, 9, size=(T, K))
+        x = xi.astype(np.float16)
+        y = ref.linear(x, lo, hi, s, z, bits)
+        wq = q.astype(np.int64) - np.repeat(z_int, 64, axis=1)
+        exact = xi.astype(np.int64) @ wq.T          # numpy int64 matmul, exact
+        assert np.array_equal(y, exact.astype(np.float64))
+
+
+def check_closed_forms():
+    rng = np.random.default_rng(11)
+    N, K, T, bits = 8, 256, 3, 4
+    q, lo, hi, s, z, x = _tiny_case(rng, N, K, T, bits)
+    # X = 0 -> Y = 0
+    assert np.all(ref.linear(np.zeros_like(x), lo, hi, s, z, bits) == 0.0)
+    # q == z -> Y = 0 (z set from the codes of each group where they are constant)
+    qc = np.repeat(rng.integers(0, 16, size=(N, K // 64)), 64, axis=1).astype(np.uint8)
+    loc, _ = pack_canonical(qc, bits)
+    zc = qc[:, ::64].astype(np.float16)
+    assert np.all(ref.linear(x, loc, None, s, zc, bits) == 0.0)
+    # X constant c on group g only -> Y[t, n] = c * s[n, g] * sum_{k in g} (q - z)
+    for g in range(K // 64):
+        c = 0.75
+        xg = np.zeros((1, K), dtype=np.float16)
+        xg[0, 64 * g:64 * (g + 1)] = c
+        y = ref.linear(xg, lo, hi, s, z, bits)[0]
+        for n in range(N):
+            want = Fraction(c) * Fraction(float(s[n, g])) * sum(
+                Fraction(int(v)) - Fraction(float(z[n, g])) for v in q[n, 64 * g:64 * (g + 1)])
+            assert abs(Fraction(float(y[n])) - want) <= abs(want) * Fraction(1, 2 ** 45) + Fraction(1, 2 ** 60)
+
+
+def check_equalisation_power_of_two():
+    """X' = X * 2^-e and scales' = scales * 2^e per group leave Y bit-identical."""
+    rng = np.random.default_rng(5)
+    for bits in (4, 5):
+        N, K, T = 16, 512, 4
+        q, lo, hi, s, z, x = _tiny_case(rng, N, K, T, bits)
+        e = rng.integers(-2, 1, size=K // 64)              # e in {-2, -1, 0}
+        x2 = (x.astype(np.float64) * np.repeat(2.0 ** (-e), 64)[None, :]).astype(np.float16)
+        s2 = (s.astype(np.float64) * (2.0 ** e)[None, :]).astype(np.float16)
+        # exactness of the rescaled inputs (no rounding happened)
+        assert np.array_equal(x2.astype(np.float64) * np.repeat(2.0 ** e, 64)[None, :],
+                              x.astype(np.float64))
+        assert np.array_equal(s2.astype(np.float64) * (2.0 ** -e)[None, :], s.astype(np.float64))
+        y1 = ref.linear(x, lo, hi, s, z, bits)
+        y2 = ref.linear(x2, lo, hi, s2, z, bits)
+        assert np.array_equal(y1, y2)
+
+
+def check_equalisation_general():
+    """Arbitrary positive per-channel factors on the dequantised weights (the identity itself)."""
+    rng = np.random.default_rng(6)
+    N, K, T, bits = 12, 256, 3, 5
+    q, lo, hi, s, z, x = _tiny_case(rng, N, K, T, bits)
+    f = rng.uniform(0.25, 4.0, size=K)
+    w = ref.dequantize(ref.unpack_codes(lo, hi, K, bits), s, z)
+    y = ref.linear(x, lo, hi, s, z, bits)
+    y_eq = (x.astype(np.float64) / f[None, :]) @ (w * f[None, :]).T
+    assert np.max(np.abs(y - y_eq)) <= 1e-12 * max(1.0, np.max(np.abs(y)))
+
+
+def check_permutations():
+    rng = np.random.default_rng(9)
+    N, K, T, bits = 16, 256, 3, 4
+    q, lo, hi, s, z, x = _tiny_case(rng, N, K, T, bits)
+    y = ref.linear(x, lo, hi, s, z, bits)
+    scale = max(1.0, float(np.max(np.abs(y))))
+    # k permutation inside each group, applied to both W and X
+    perm = np.concatenate([64 * g + rng.permutation(64) for g in range(K // 64)])
+    lo_p, _ = pack_canonical(q[:, perm], bits)
+    y_p = ref.linear(x[:, perm], lo_p, None, s, z, bits)
+    assert np.max(np.abs(y - y_p)) <= 1e-13 * scale
+    # whole-group permutation with their scales and zeros
+    gp = rng.permutation(K // 64)
+    cols = np.concatenate([np.arange(64 * g, 64 * (g + 1)) for g in gp])
+    lo_g, _ = pack_canonical(q[:, cols], bits)
+    y_g = ref.linear(x[:, cols], lo_g, None, s[:, gp], z[:, gp], bits)
+    assert np.max(np.abs(y - y_g)) <= 1e-13 * scale
+    # row permutation permutes the output columns exactly
+    rp = rng.permutation(N)
+    y_r = ref.linear(x, lo[rp], None, s[rp], z[rp], bits)
+    assert np.array_equal(y_r, y[:, rp])
+    # token independence: a row of Y depends only on the same row of X
+    x2 = x.copy()
+    x2[1] = np.float16(np.nan)
+    y2 = ref.linear(x2, lo, hi, s, z, bits)
+    assert np.array_equal(y2[[0, 2]], y[[0, 2]])
+    assert np.all(np.isnan(y2[1]))
+
+
+def check_silu_and_swiglu():
+    a = np.array([-60.0, -5.0, -1.0, 0.0, 1e-3, 1.0, 3.0, 60.0])
+    got = ref.silu(a)
+    want = a * scipy.special.expit(a)
+    assert np.max(np.abs(got - want)) <= 1e-15 * np.maximum(1.0, np.abs(want)).max()
+    assert abs(ref.silu(np.array([1.0]))[0] - 0.7310585786300049) < 1e-15
+    assert abs(ref.silu(np.array([-1.0]))[0] + 0.2689414213699951) < 1e-15
+    assert ref.silu(np.array([0.0]))[0] == 0.0
+    # crafted gate/up rows: G = 1, U = 2 exactly -> out = 2 * silu(1)
+    K = 64
+    qg = np.zeros((1, K), dtype=np.uint8)
+    qg[0, 0] = 9                     # s=1, z=8 -> w = 1 at k=0
+    qu = np.zeros((1, K), dtype=np.uint8)
+    qu[0, 0] = 10                    # w = 2 at k=0
+    s = np.ones((1, 1), dtype=np.float16)
+    z = np.full((1, 1), 8, dtype=np.float16)
+    x = np.zeros((1, K), dtype=np.float16)
+    x[0, 0] = 1.0
+    lg, _ = pack_canonical(qg, 4)
+    lu, _ = pack_canonical(qu, 4)
+    out = ref.swiglu(x, (lg, None, s, z), (lu, None, s, z), bits=4)
+    assert abs(out[0, 0] - 2 * 0.7310585786300049) < 1e-15
+    # the gate goes through silu, the up projection does not (swap -> different)
+    out_sw = ref.swiglu(x, (lu, None, s, z), (lg, None, s, z), bits=4)
+    assert abs(out_sw[0, 0] - 1 * 2 * scipy.special.expit(2.0)) < 1e-15
+
+
+def check_linear_add():
+    rng = np.random.default_rng(13)
+    N, K, T, bits = 8, 128, 3, 5
+    q, lo, hi, s, z, x = _tiny_case(rng, N, K, T, bits)
+    r = rng.standard_normal((T, N)).astype(np.float16)
+    out0 = ref.linear_add(np.zeros_like(x), lo, hi, s, z, r, bits)
+    assert np.array_equal(out0, r.astype(np.float64))
+    out = ref.linear_add(x, lo, hi, s, z, r, bits)
+    y = ref.linear(x, lo, hi, s, z, bits)
+    assert np.array_equal(out, y + r.astype(np.float64))
+
+
+ALL_CHECKS = [
+    check_unpack_fixtures, check_hand_dequant, check_bruteforce_exact,
+    check_integer_special_case, check_closed_forms, check_equalisation_power_of_two,
+    check_equalisation_general, check_permutations, check_silu_and_swiglu, check_linear_add,
+]
+
+
+# ---------------------------------------------------------------- tests
+
+@pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda c: c.__name__)
+def test_pin(check):
+    check()
+
+
+def test_generator_packs_fixtures():
+    """The shared generator writes the hand-written canonical bytes."""
+    for bits, K, lo, hi, codes in _read_code_fixtures():
+        lo2, hi2 = pack_canonical(codes.astype(np.uint8)[None, :], bits)
+        assert np.array_equal(lo2, lo)
+        if hi is None:
+            assert hi2 is None
+        else:
+            assert np.array_equal(hi2, hi)
+
+
+def test_rel_l2_and_round():
+    assert oracle.rel_l2(np.array([1.0, 0.0]), np.array([1.0, 0.0])) == 0.0
+    assert abs(oracle.rel_l2(np.array([3.0, 4.0]), np.array([0.0, 5.0])) - np.sqrt(10.0) / 5.0) < 1e-15
+    assert oracle.fp16_round(np.array([1.0 + 2.0 ** -11]))[0] == np.float16(1.0)  # ties to even
+    assert oracle.fp16_round(np.array([1.0 + 3 * 2.0 ** -11]))[0] == np.float16(1.0 + 2.0 ** -9)
+
+
+# --- planted mistakes: each must make at least one pin fail
+
+def _mut_nibble_order(lo, hi, K, bits):
+    q = _orig_unpack(lo, hi, K, bits)
+    lo4, h = q & 15, q & 16
+    q2 = q.copy()
+    q2[:, 0::2] = lo4[:, 1::2] | h[:, 0::2]
+    q2[:, 1::2] = lo4[:, 0::2] | h[:, 1::2]
+    return q2
+
+
+def _mut_hi_bit_order(lo, hi, K, bits):
+    q = _orig_unpack(lo, hi, K, bits)
+    if bits == 5:
+        q = q & 15
+        hi = np.asarray(hi, dtype=np.uint8)
+        for i in range(8):
+            q[:, i::8] += ((hi >> (7 - i)) & 1).astype(np.int64) << 4
+    return q
+
+
+def _mut_zero_sign(q, scales, zeros, group=64):
+    return _orig_dequant(q, scales, -np.asarray(zeros, dtype=np.float64), group)
+
+
+def _mut_group_tiled(q, scales, zeros, group=64):
+    # np.tile instead of np.repeat: column k takes group k % G instead of k // 64
+    s = np.tile(np.asarray(scales, np.float64), (1, group))
+    z = np.tile(np.asarray(zeros, np.float64), (1, group))
+    return s * (q - z)
+
+
+def _mut_group_offbyone(q, scales, zeros, group=64):
+    s = np.roll(np.asarray(scales, np.float64), 1, axis=1)
+    z = np.asarray(zeros, np.float64)
+    return np.repeat(s, group, axis=1) * (q - np.repeat(z, group, axis=1))
+
+
+def _mut_zero_scaled(q, scales, zeros, group=64):
+    # offset applied after the scale: s*q - z
+    s = np.repeat(np.asarray(scales, np.float64), group, axis=1)
+    z = np.repeat(np.asarray(zeros, np.float64), group, axis=1)
+    return s * q - z
+
+
+def _mut_silu_sign(a):
+    a = np.asarray(a, dtype=np.float64)
+    return a / (1.0 + np.exp(a))
+
+
+def _mut_no_residual(x, lo, hi, scales, zeros, r, bits, group=64):
+    return _orig_linear(x, lo, hi, scales, zeros, bits, group)
+
+
+def _mut_transposed_rows(x, lo, hi, scales, zeros, bits, group=64, n_chunk=2048):
+    y = _orig_linear(x, lo, hi, scales, zeros, bits, group, n_chunk)
+    return y[:, ::-1].copy()
+
+
+_orig_unpack = ref.unpack_codes
+_orig_dequant = ref.dequantize
+_orig_linear = ref.linear
+
+MUTATIONS = {
+    "nibble_order": ("unpack_codes", _mut_nibble_order),
+    "hi_bit_order": ("unpack_codes", _mut_hi_bit_order),
+    "zero_sign": ("dequantize", _mut_zero_sign),
+    "group_tiled": ("dequantize", _mut_group_tiled),
+    "group_index_off_by_one": ("dequantize", _mut_group_offbyone),
+    "zero_after_scale": ("dequantize", _mut_zero_scaled),
+    "silu_sign": ("silu", _mut_silu_sign),
+    "dropped_residual": ("linear_add", _mut_no_residual),
+    "reversed_rows": ("linear", _mut_transposed_rows),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes_are_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(ref, attr, fn)
+    failed = []
+    for check in ALL_CHECKS:
+        try:
+            check()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(check.__name__)
+    assert failed, f"planted mistake {name!r} passed every pin"

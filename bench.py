@@ -1,0 +1,282 @@
+#!/usr/bin/env python3
+"""Benchmark of the groupwise W4 dequantize-GEMM on one MI355X; prints ONE JSON line.
+
+Default workload (the decode / MTP-verify configuration): W4 weights N=12288 x K=5120, one
+fp16 scale and zero per 64 columns, codes uniform 0..15, zero-points uniform 6..9, scales
+uniform [0.005, 0.02], X ~ N(0, 1) fp16.  A step is one call at each verify width
+T = 1, 2 and 4 (three launches, each through the public ``w4_linear`` and the route table).
+
+Cold weights: every weight set here fits in MI355X's 256 MB Infinity Cache, so each launch
+reads the next of C >= 1 GiB / W-stream device copies of the packed weights (the cold regime
+of the ninfer-3080 performance notes, "Route boundaries are measured here").  Activations stay
+resident, as when produced by the previous op.
+
+value = effective weight-stream GB/s over the timed steps (packed codes + fp16 scales + fp16
+zeros per launch, times launches, divided by the timed wall time).  Per-launch kernel durations
+come from HIP events recorded on the launch stream around every launch in the timed region;
+the dominant launch's algorithmic bytes over its mean duration gives roofline.achieved.
+
+cpu_baseline times the fp64 oracle on the host cores over repeats of the same step (about
+10-30 s); it is a reference point, not a target.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix, published
+
+WORKLOADS = {
+    # name: (synth config, widths per step, op)
+    "decode": ("decode", (1, 2, 4), "linear"),
+    "batched": ("batched", (8, 16, 32, 64), "linear"),
+    "swiglu": ("swiglu", (1, 4, 16, 64), "swiglu"),
+    "prefill": ("prefill", (1024, 4096), "add"),
+}
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4_groupwise_gemm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload: str, T: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it still
+    describes the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha") != kernel_source_sha():
+        return None
+    v = rec.get("bytes_per_launch", {}).get(str(T))
+    return None if v is None else float(v)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of rotated weight copies")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--route", type=int, default=-1, help="force one route (bench of a schedule)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path (each GPU runs the "
+              "same kernels on its own shard); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+    import w4_groupwise_gemm_amd as w4
+    from synth import make_workload
+
+    cfg_name, widths, opname = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {cfg_name}", file=sys.stderr, flush=True)
+    wl = make_workload(cfg_name)
+    bits = wl.weights[0].bits
+    K = wl.weights[0].K
+    if opname == "swiglu":
+        g, u = wl.weights
+        packed = w4.repack_pair((g.lo, g.hi, g.scales, g.zeros), (u.lo, u.hi, u.scales, u.zeros), bits)
+        N, pair, op = g.N, True, w4.OP_SWIGLU
+        rows = 2 * N
+    else:
+        if len(wl.weights) > 1:  # parents sharing one activation: one N-concatenated matrix
+            lo = np.concatenate([ws.lo for ws in wl.weights])
+            sc = np.concatenate([ws.scales for ws in wl.weights])
+            ze = np.concatenate([ws.zeros for ws in wl.weights])
+            hi = None if bits == 4 else np.concatenate([ws.hi for ws in wl.weights])
+        else:
+            ws = wl.weights[0]
+            lo, hi, sc, ze = ws.lo, ws.hi, ws.scales, ws.zeros
+        packed = w4.repack(lo, hi, sc, ze, bits)
+        N, pair = lo.shape[0], False
+        op = w4.OP_ADD if opname == "add" else w4.OP_LINEAR
+        rows = N
+    wstream = sum(int(a.nbytes) for a in packed)  # codes + scales + zeros as laid out
+    wstream_alg = rows * K * bits // 8 + rows * (K // 64) * 4
+    copies = max(2, int(np.ceil(args.cold_bytes * (1 << 30) / wstream)))
+    print(f"[bench] {copies} cold copies of {wstream / 1e6:.2f} MB", file=sys.stderr, flush=True)
+    pws = [w4.to_device(packed, N, K, bits, pair, device=dev) for _ in range(copies)]
+    x_all = torch.from_numpy(wl.x).to(dev)
+    xs = {T: x_all[:T].contiguous() for T in widths}
+    res = {T: torch.from_numpy(wl.r[:T]).to(dev) for T in widths} if wl.r is not None else {}
+    outs = {T: torch.empty((T, N), dtype=torch.float16, device=dev) for T in widths}
+
+    def call(T, pw):
+        if args.route >= 0:
+            return w4.linear_route(args.route, op, xs[T], pw, residual=res.get(T), out=outs[T])
+        if op == w4.OP_SWIGLU:
+            return w4.linear_swiglu(xs[T], pw, out=outs[T])
+        if op == w4.OP_ADD:
+            return w4.linear_add(xs[T], pw, res[T], out=outs[T])
+        return w4.linear(xs[T], pw, out=outs[T])
+
+    # ---- parity gate in the same run (sampled output columns vs the fp64 oracle)
+    import oracle
+    rng = np.random.default_rng(0)
+    parity = {}
+    for T in widths:
+        call(T, pws[0])
+        torch.cuda.synchronize()
+        y = outs[T].cpu().numpy().astype(np.float64)
+        if op == w4.OP_SWIGLU:
+            cols = np.sort(rng.choice(N, 256, replace=False))
+            g, u = wl.weights
+            gref = oracle.linear_rows(wl.x[:T], g.lo, g.hi, g.scales, g.zeros, bits, cols)
+            uref = oracle.linear_rows(wl.x[:T], u.lo, u.hi, u.scales, u.zeros, bits, cols)
+            ref = oracle.silu(gref) * uref
+        else:
+            cols = np.sort(rng.choice(N, 256, replace=False))
+            ref = oracle.linear_rows(wl.x[:T], lo, hi, sc, ze, bits, cols)
+            if op == w4.OP_ADD:
+                ref = ref + wl.r[:T][:, cols].astype(np.float64)
+        got = y[:, cols]
+        rel = oracle.rel_l2(got, ref)
+        elem = float(np.max(np.abs(got - ref) / (1.0 + np.abs(ref))))
+        parity[str(T)] = {"rel_l2": rel, "max_elem": elem, "ok": bool(rel <= 2e-3 and elem <= 1e-2)}
+    parity_ok = all(p["ok"] for p in parity.values())
+    print(f"[bench] parity {parity}", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ci = 0
+    for _ in range(args.warmup):
+        for T in widths:
+            call(T, pws[ci % copies])
+            ci += 1
+    torch.cuda.synchronize()
+
+    n_launch = args.steps * len(widths)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_launch)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    li = 0
+    for _ in range(args.steps):
+        for T in widths:
+            ev[li][0].record(stream)
+            call(T, pws[ci % copies])
+            ev[li][1].record(stream)
+            ci += 1
+            li += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_T = {}
+    for i, T in enumerate(widths):
+        d = np.array([ev[s * len(widths) + i][0].elapsed_time(ev[s * len(widths) + i][1])
+                      for s in range(args.steps)]) * 1e3  # us
+        alg_bytes = wstream_alg + T * K * 2 + T * N * 2 * (2 if op == w4.OP_ADD else 1)
+        flops = 2.0 * T * rows * K
+        rid = args.route if args.route >= 0 else w4.route_for(op, bits, T, N, K)
+        boot = np.median(rng.choice(d, size=(1000, d.size)), axis=1)
+        per_T[str(T)] = {
+            "route": w4.route_name(rid), "us_mean": float(d.mean()), "us_median": float(np.median(d)),
+            "us_ci95": [float(np.percentile(boot, 2.5)), float(np.percentile(boot, 97.5))],
+            "weight_GBs": wstream_alg / (d.mean() * 1e3), "alg_GBs": alg_bytes / (d.mean() * 1e3),
+            "TFLOPs": flops / (d.mean() * 1e6), "alg_bytes": alg_bytes,
+        }
+    dom = max(widths, key=lambda T: per_T[str(T)]["us_mean"])
+    pd = per_T[str(dom)]
+    prefill = min(widths) >= 1024
+    if prefill:
+        achieved, peak, unit, bound = pd["TFLOPs"], MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = pd["alg_GBs"], HBM_PEAK_GBS, "GB/s", "hbm"
+    traffic = traffic_from_profiles(args.workload, dom)
+    roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+                "frac": achieved / peak, "traffic": traffic,
+                "kernel": f"T={dom} {pd['route']}", "alg_bytes_per_launch": pd["alg_bytes"],
+                "us_per_launch": pd["us_mean"]}
+
+    ms_per_step = wall * 1e3 / args.steps
+    if prefill:
+        metric = "W5 LinearAdd MFMA TFLOP/s (T>=1024)"
+        value = sum(2.0 * T * rows * K for T in widths) / (ms_per_step * 1e9)
+        unit_v = "TFLOP/s"
+    else:
+        metric = "W4 GEMM effective weight GB/s (T<=64)"
+        value = len(widths) * wstream_alg / (ms_per_step * 1e6)
+        unit_v = "GB/s"
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, widths, op, bits, lo if not pair else None, hi if not pair else None,
+                           sc if not pair else None, ze if not pair else None, wstream_alg, prefill,
+                           rows, K)
+
+    line = {
+        "metric": metric, "value": value, "unit": unit_v, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {'SwiGLU pair ' if pair else ''}W{bits} N={N} "
+                               f"K={K} group=64, T in {list(widths)}, cold ({copies} copies)",
+                   "N": N, "K": K, "bits": bits, "T": list(widths), "op": opname,
+                   "cold_copies": copies, "parallelism": "none (1 GPU)"},
+        "parity_ok": parity_ok, "parity": parity, "per_T": per_T,
+        "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+    return 0 if parity_ok else 1
+
+
+def cpu_baseline(wl, widths, op, bits, lo, hi, sc, ze, wstream_alg, prefill, rows, K):
+    """The fp64 oracle on the host cores, on a bounded sample of the same step."""
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    if prefill:
+        # one token chunk of 64 over the full weight: scaled by FLOPs
+        T = 64
+        t0 = time.perf_counter()
+        y = oracle.linear(wl.x[:T], lo, hi, sc, ze, bits)
+        if op == 2:
+            y = y + wl.r[:T].astype(np.float64)
+        dt = time.perf_counter() - t0
+        return {"value": 2.0 * T * rows * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+                "kind": "oracle", "sample": f"T={T} tokens over the full {rows}x{K} weight, "
+                                             f"{dt:.1f} s"}
+    reps, total, t_start = 0, 0.0, time.perf_counter()
+    while True:
+        for T in widths:
+            if op == 1:
+                g, u = wl.weights
+                oracle.swiglu(wl.x[:T], (g.lo, g.hi, g.scales, g.zeros),
+                              (u.lo, u.hi, u.scales, u.zeros), bits=bits)
+            else:
+                oracle.linear(wl.x[:T], lo, hi, sc, ze, bits)
+        reps += 1
+        total = time.perf_counter() - t_start
+        if total >= 10.0 or reps >= 20:
+            break
+    return {"value": reps * len(widths) * wstream_alg / total / 1e9, "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full steps (T in {list(widths)}), {total:.1f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,158 @@
+/*
+ * w4gemm.h -- C ABI of the groupwise low-bit dequantize + matrix multiply library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ *   Y[T, N] = X[T, K] . dequant(Wq)[N, K]^T,   dequant(Wq)[n, k] = s[n, g] * (q[n, k] - z[n, g]),
+ *   g = k / 64,  q in [0, 2^bits),  bits in {4, 5}.
+ *
+ * Sources.  The operation is the fused kernel of ARK research "Fused kernels" (section "Why
+ * standard kernels stall": unpack the low-bit weights and multiply in one pass shaped for a
+ * batch) and of the ninfer-3080 performance notes (sections "What changed" and "A8 prefill
+ * routes": Q4/Q5 groupwise projections, the gate_up SwiGLU pair and the LinearAdd op, one
+ * scale per 64 columns per the "cuBLAS prefill route" section).  The pages give no zero-point
+ * rule, no dtype for activations and no signature; this library reads them as: zero-point z
+ * in code units (w = s * (q - z)), fp16 activations/scales/zero-points/outputs, fp32
+ * accumulation, one round-to-nearest-even rounding of each output.
+ *
+ * Conventions shared by every entry point:
+ *   - fp16 tensors are passed as uint16_t bit patterns.
+ *   - Device pointers are owned by the caller; the library never allocates, frees or keeps
+ *     them.  Host pointers (repack) are likewise the caller's.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Compute calls validate every
+ *     argument synchronously first, then enqueue exactly one kernel on `stream` and return
+ *     without synchronising: they are asynchronous and may be captured into a HIP graph.
+ *   - On any error the call returns a negative w4_status before touching device memory;
+ *     `out` is left untouched.
+ *   - The library is stateless apart from a per-device "is gfx950" cache, so concurrent calls
+ *     on different streams are safe.
+ */
+#ifndef W4GEMM_H
+#define W4GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define W4_LAYOUT_VERSION 1
+
+typedef enum {
+  W4_OK = 0,
+  W4_ERR_INVALID_ARG = -1, /* null pointer, negative or zero size, N % 16 or K % 64 not 0   */
+  W4_ERR_UNSUPPORTED = -2, /* bits not in {4,5}, group != 64, unknown op                    */
+  W4_ERR_MISALIGNED = -3,  /* a pointer is not 16-byte aligned                              */
+  W4_ERR_ALIAS = -4,       /* out overlaps an input (out == residual exactly is allowed)    */
+  W4_ERR_DOMAIN = -5,      /* route forced outside its T domain, or route id unknown        */
+  W4_ERR_DEVICE = -6,      /* current device is not gfx950, or no device                    */
+  W4_ERR_LAUNCH = -7       /* the kernel launch failed                                       */
+} w4_status;
+
+/* op codes for w4_route_for / w4_linear_route */
+#define W4_OP_LINEAR 0
+#define W4_OP_SWIGLU 1
+#define W4_OP_ADD 2
+
+/* ------------------------------------------------------------------------------------------
+ * Canonical (user-side) weight format -- what w4_repack reads.
+ *   4-bit: lo  uint8 [N][K/2]; code(n,k) = (lo[n][k/2] >> (4*(k&1))) & 0xF (even k = low nibble)
+ *   5-bit: lo as above holds bits 0..3; hi uint8 [N][K/8] holds bit 4:
+ *          (hi[n][k/8] >> (k&7)) & 1  (the 4-bit plane + high-bit plane of the ninfer-3080
+ *          performance notes, "What changed", Q5 bullet).
+ *   scales, zeros: fp16 [N][K/64].
+ *
+ * Packed (device) layout -- what the compute calls read.  Row tiles of 16 rows, k-blocks of
+ * 128 columns, KB = ceil(K/128).  Byte image of one (row tile rt, k-block kb) block:
+ *   4-bit: 1024 B = 64 lanes x 16 B.      5-bit: 1280 B = 64 lanes x 16 B (low plane), then
+ *                                                 64 lanes x 4 B (high plane).
+ *   blocks are stored rt-major: offset = (rt * KB + kb) * block_bytes.
+ *   Lane l serves row 16*rt + (l % 16); its lane group is g = l / 16.  Dword j (0..3) of the
+ *   lane's 16 low-plane bytes holds 8 codes, slots e = 0..7, for
+ *       k = 128*kb + 64*(j>>1) + 16*g + 8*(j&1) + e,
+ *   slot e in bits [4*(e>>1) + 16*(e&1), +4).  Dwords 0,1 lie in group 2*kb and 2,3 in group
+ *   2*kb+1, so every 32-k matrix-core step stays inside one group; inside a group the k order
+ *   is permuted, which leaves the product unchanged when activations follow the same order
+ *   (ninfer-3080 performance notes, "What changed", "Permuted k order").
+ *   5-bit high plane: the lane's 32-bit word holds bit 4 of slot e of dword j at bit
+ *       t_j + r_e,  t = {0, 2, 8, 10},  r = {0, 16, 4, 20, 1, 17, 5, 21}.
+ *   scales / zeros: fp16 [N/16][KB][16][2]; element (rt, kb, r, h) = value of row 16*rt + r,
+ *   group 2*kb + h.
+ *   When K % 128 == 64 the second group of the last k-block is padding: codes 0, scale 0,
+ *   zero 0.  Repacking is a bit-exact permutation plus that zero padding.
+ *   The packed form of a row-concatenation [A; B] (same K, bits) is the byte concatenation of
+ *   the packed forms of A and B, so parents that share one activation can be packed into one
+ *   buffer and run as one call.
+ *   SwiGLU pair layout (w4_repack_pair): packed row tile 2i = gate rows 16i..16i+15 and
+ *   packed row tile 2i+1 = up rows 16i..16i+15, i.e. a packed matrix of 2N rows.
+ * ---------------------------------------------------------------------------------------- */
+
+/* Bytes of the packed code buffer for an N x K matrix; 0 if the shape is invalid. */
+size_t w4_packed_bytes(int N, int K, int bits, int group);
+
+/* Bytes of EACH of the packed scales and zeros buffers; 0 if the shape is invalid. */
+size_t w4_packed_sz_bytes(int N, int K, int group);
+
+/* Repack one matrix from the canonical format (host memory in, host memory out).
+ * codes_hi must be NULL for bits == 4 and non-NULL for bits == 5.  Output buffers must hold
+ * w4_packed_bytes / w4_packed_sz_bytes bytes.  Pure permutation: bit-exact, deterministic. */
+int w4_repack(const uint8_t* codes_lo, const uint8_t* codes_hi, const uint16_t* scales,
+              const uint16_t* zeros, int N, int K, int bits, int group, void* w_out,
+              uint16_t* scales_out, uint16_t* zeros_out);
+
+/* Repack a gate/up pair (each N x K, canonical, host) into the interleaved pair layout used by
+ * w4_linear_swiglu.  Outputs hold w4_packed_bytes(2N,...) and w4_packed_sz_bytes(2N,...). */
+int w4_repack_pair(const uint8_t* gate_lo, const uint8_t* gate_hi, const uint16_t* gate_scales,
+                   const uint16_t* gate_zeros, const uint8_t* up_lo, const uint8_t* up_hi,
+                   const uint16_t* up_scales, const uint16_t* up_zeros, int N, int K, int bits,
+                   int group, void* w_pair_out, uint16_t* scales_pair_out,
+                   uint16_t* zeros_pair_out);
+
+/* out[T][N] = fp16_rne(X . dequant(W)^T).  x: fp16 [T][K] row-major, device.  w, scales, zeros:
+ * w4_repack output, device.  out: fp16 [T][N], device.  T == 0 is a successful no-op.
+ * Any T >= 1 is accepted; rows of x beyond T-1 are never read and rows of out beyond T-1
+ * are never written. */
+int w4_linear(const uint16_t* x, const void* w, const uint16_t* scales, const uint16_t* zeros,
+              int T, int N, int K, int bits, int group, uint16_t* out, void* stream);
+
+/* out[T][N] = fp16_rne(silu(X . Wg^T) * (X . Wu^T)), silu(a) = a / (1 + exp(-a)), in fp32.
+ * N is the width of EACH of gate and up; w_pair/scales_pair/zeros_pair are w4_repack_pair
+ * output (2N packed rows).  The gate_up pair of the ninfer-3080 performance notes ("The token
+ * tile, and why it was hiding"). */
+int w4_linear_swiglu(const uint16_t* x, const void* w_pair, const uint16_t* scales_pair,
+                     const uint16_t* zeros_pair, int T, int N, int K, int bits, int group,
+                     uint16_t* out, void* stream);
+
+/* out[T][N] = fp16_rne(X . dequant(W)^T + R) with the add in fp32 (the LinearAdd op of the
+ * ninfer-3080 performance notes, "A8 prefill routes" table).  residual: fp16 [T][N].
+ * out == residual (exactly) is allowed: each element is read before it is written, once. */
+int w4_linear_add(const uint16_t* x, const void* w, const uint16_t* scales, const uint16_t* zeros,
+                  const uint16_t* residual, int T, int N, int K, int bits, int group,
+                  uint16_t* out, void* stream);
+
+/* ---- routes: every op has several kernels ("schedules"), each with an explicit T domain
+ * (ninfer-3080 performance notes, "Route boundaries are measured here").  The three calls
+ * above pick exactly one route with w4_route_for and launch it once. */
+
+/* Route id chosen for (op, bits, T, N, K), or a negative w4_status. */
+int w4_route_for(int op, int bits, int T, int N, int K);
+
+/* Run a specific route; W4_ERR_DOMAIN if T lies outside its domain.  residual is ignored
+ * unless op == W4_OP_ADD.  Same argument meaning and validation as the op's own call. */
+int w4_linear_route(int route_id, int op, const uint16_t* x, const void* w,
+                    const uint16_t* scales, const uint16_t* zeros, const uint16_t* residual,
+                    int T, int N, int K, int bits, int group, uint16_t* out, void* stream);
+
+int w4_route_count(void);
+const char* w4_route_name(int route_id); /* NULL for an unknown id */
+/* T domain [*tmin, *tmax] of a route; W4_ERR_DOMAIN for an unknown id. */
+int w4_route_domain(int route_id, int* tmin, int* tmax);
+
+const char* w4_status_str(int status);
+int w4_layout_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4GEMM_H */

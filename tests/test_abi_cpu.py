@@ -1,0 +1,218 @@
+"""CPU tier: the C-ABI library loads, exports what the header declares, validates arguments
+synchronously (no device work) and repacks bit-exactly against an independent layout model."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import w4_groupwise_gemm_amd as w4
+from synth import make_weights, pack_canonical
+from layout_spec import spec_pack, spec_unpack
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4gemm.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = w4.lib()
+    names = header_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(w4.EXPORTS)
+
+
+def test_layout_version_and_status_strings():
+    assert w4.layout_version() == 1
+    for st in range(0, -8, -1):
+        assert w4.status_str(st) and w4.status_str(st) != "unknown status"
+    assert w4.status_str(-99) == "unknown status"
+
+
+def test_route_table_domains_cover_every_width():
+    n = w4.route_count()
+    assert n >= 5
+    names = [w4.route_name(i) for i in range(n)]
+    assert len(set(names)) == n and all(names)
+    assert w4.route_name(n) is None and w4.route_name(-1) is None
+    for op in (w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD):
+        for bits in (4, 5):
+            for T in list(range(1, 130)) + [255, 256, 1000, 1024, 1025, 4096, 65536]:
+                r = w4.route_for(op, bits, T, 4096, 5120)
+                assert 0 <= r < n
+                lo, hi = w4.route_domain(r)
+                assert lo <= T <= hi, (op, bits, T, r)
+
+
+def test_route_for_rejects_bad_shapes():
+    assert w4.route_for(7, 4, 1, 256, 512) == -2
+    assert w4.route_for(0, 3, 1, 256, 512) == -2
+    assert w4.route_for(0, 4, 1, 250, 512) == -1
+    assert w4.route_for(0, 4, 1, 256, 500) == -1
+    assert w4.route_for(0, 4, -1, 256, 512) == -1
+
+
+# ---- synchronous validation: fake addresses are fine because nothing touches the device
+
+def _call(fn, x=0x10000, w=0x20000000, s=0x30000000, z=0x40000000, T=4, N=256, K=512, bits=4,
+          group=64, out=0x50000000, res=None):
+    L = w4.lib()
+    if fn == "add":
+        return L.w4_linear_add(x, w, s, z, res if res is not None else 0x60000000, T, N, K, bits,
+                               group, out, None)
+    if fn == "swiglu":
+        return L.w4_linear_swiglu(x, w, s, z, T, N, K, bits, group, out, None)
+    return L.w4_linear(x, w, s, z, T, N, K, bits, group, out, None)
+
+
+@pytest.mark.parametrize("fn", ["linear", "swiglu", "add"])
+def test_validation_errors(fn):
+    assert _call(fn, bits=3) == -2
+    assert _call(fn, bits=8) == -2
+    assert _call(fn, group=32) == -2
+    assert _call(fn, group=128) == -2
+    assert _call(fn, N=250) == -1
+    assert _call(fn, N=0) == -1
+    assert _call(fn, K=500) == -1
+    assert _call(fn, K=0) == -1
+    assert _call(fn, T=-1) == -1
+    assert _call(fn, x=0) == -1
+    assert _call(fn, w=0) == -1
+    assert _call(fn, s=0) == -1
+    assert _call(fn, z=0) == -1
+    assert _call(fn, out=0) == -1
+    assert _call(fn, x=0x10008) == -3
+    assert _call(fn, w=0x20000004) == -3
+    assert _call(fn, out=0x50000002) == -3
+    # out overlapping x / w / scales
+    assert _call(fn, out=0x10000 + 16) == -4
+    assert _call(fn, out=0x20000000 + 1024) == -4
+    assert _call(fn, out=0x30000000 + 16) == -4
+    # T == 0 is a successful no-op, even with null pointers
+    assert _call(fn, T=0, x=0, w=0, s=0, z=0, out=0) == 0
+
+
+def test_linear_add_aliasing_rules():
+    # out == residual exactly is allowed (validation passes; no GPU here so the device check
+    # is what fails) -- partial overlap is an alias error
+    assert _call("add", res=0x50000000 + 16) == -4
+    assert _call("add", res=0) == -1
+    assert _call("add", res=0x60000008) == -3
+
+
+def test_forced_route_outside_domain():
+    L = w4.lib()
+    args = (0x10000, 0x20000000, 0x30000000, 0x40000000, None)
+    n = w4.route_count()
+    assert L.w4_linear_route(n, 0, *args, 4, 256, 512, 4, 64, 0x50000000, None) == -5
+    assert L.w4_linear_route(-1, 0, *args, 4, 256, 512, 4, 64, 0x50000000, None) == -5
+    for r in range(n):
+        lo, hi = w4.route_domain(r)
+        if hi < 1 << 24:
+            assert L.w4_linear_route(r, 0, *args, hi + 1, 256, 512, 4, 64, 0x50000000, None) == -5
+
+
+def test_packed_sizes():
+    assert w4.packed_bytes(256, 512, 4) == 256 * 512 // 2
+    assert w4.packed_bytes(256, 512, 5) == 256 * 512 * 5 // 8
+    assert w4.packed_bytes(16, 64, 4) == 1024                 # half-empty k-block is padded
+    assert w4.packed_sz_bytes(256, 512) == 256 * 512 // 64 * 2
+    assert w4.packed_sz_bytes(16, 64) == 16 * 2 * 2
+    assert w4.packed_bytes(250, 512, 4) == 0
+    assert w4.packed_bytes(256, 500, 4) == 0
+    assert w4.packed_bytes(256, 512, 6) == 0
+    assert w4.packed_bytes(256, 512, 4) == w4.lib().w4_packed_bytes(256, 512, 4, 64)
+    assert w4.lib().w4_packed_bytes(256, 512, 4, 32) == 0
+
+
+# ---- repacking: C++ vs the independent layout model, and round trips
+
+@pytest.mark.parametrize("bits", [4, 5])
+@pytest.mark.parametrize("N,K", [(16, 64), (16, 128), (32, 192), (48, 512), (16, 320)])
+def test_repack_matches_spec(bits, N, K):
+    rng = np.random.default_rng(N * 1000 + K + bits)
+    ws = make_weights(rng, "w", N, K, bits, ("real", 0, 1 << bits), (0.001, 0.05))
+    w, s, z = w4.repack(ws.lo, ws.hi, ws.scales, ws.zeros, bits)
+    w2, s2, z2 = spec_pack(ws.q.astype(np.int64), ws.scales, ws.zeros, bits)
+    assert np.array_equal(w, w2)
+    assert np.array_equal(s, s2)
+    assert np.array_equal(z, z2)
+    q, su, zu = spec_unpack(w, s, z, N, K, bits)
+    assert np.array_equal(q, ws.q.astype(np.int64))
+    assert np.array_equal(su, ws.scales.view(np.uint16))
+    assert np.array_equal(zu, ws.zeros.view(np.uint16))
+
+
+@pytest.mark.parametrize("bits", [4, 5])
+def test_repack_every_code_every_slot(bits):
+    """Each code value at each (lane, dword, slot) position survives the round trip."""
+    N, K = 16, 128
+    nv = 1 << bits
+    for shift in range(nv):
+        q = ((np.arange(N * K).reshape(N, K) + shift) % nv).astype(np.uint8)
+        lo, hi = pack_canonical(q, bits)
+        s = np.ones((N, K // 64), dtype=np.float16)
+        z = np.zeros((N, K // 64), dtype=np.float16)
+        w, sp, zp = w4.repack(lo, hi, s, z, bits)
+        qq, _, _ = spec_unpack(w, sp, zp, N, K, bits)
+        assert np.array_equal(qq, q.astype(np.int64))
+
+
+@pytest.mark.parametrize("bits", [4, 5])
+def test_repack_pair_interleaves_row_tiles(bits):
+    rng = np.random.default_rng(3)
+    N, K = 48, 256
+    g = make_weights(rng, "g", N, K, bits, ("uniform", 6, 9), (0.005, 0.02))
+    u = make_weights(rng, "u", N, K, bits, ("uniform", 6, 9), (0.005, 0.02))
+    w, s, z = w4.repack_pair((g.lo, g.hi, g.scales, g.zeros), (u.lo, u.hi, u.scales, u.zeros), bits)
+    # expected: packed rows = [g tile 0, u tile 0, g tile 1, u tile 1, ...]
+    rows = []
+    for i in range(N // 16):
+        rows.append(np.arange(16 * i, 16 * i + 16))
+    qi = np.concatenate([np.concatenate([g.q[r], u.q[r]]) for r in rows])
+    si = np.concatenate([np.concatenate([g.scales[r], u.scales[r]]) for r in rows])
+    zi = np.concatenate([np.concatenate([g.zeros[r], u.zeros[r]]) for r in rows])
+    w2, s2, z2 = spec_pack(qi.astype(np.int64), si, zi, bits)
+    assert np.array_equal(w, w2) and np.array_equal(s, s2) and np.array_equal(z, z2)
+
+
+def test_repack_concat_is_byte_concat():
+    """Packing a row-concatenation equals concatenating the packed parts (shared-X parents)."""
+    rng = np.random.default_rng(4)
+    a = make_weights(rng, "a", 32, 256, 4, ("uniform", 6, 9), (0.005, 0.02))
+    b = make_weights(rng, "b", 48, 256, 4, ("uniform", 6, 9), (0.005, 0.02))
+    pa = w4.repack(a.lo, None, a.scales, a.zeros, 4)
+    pb = w4.repack(b.lo, None, b.scales, b.zeros, 4)
+    pc = w4.repack(np.concatenate([a.lo, b.lo]), None, np.concatenate([a.scales, b.scales]),
+                   np.concatenate([a.zeros, b.zeros]), 4)
+    for i in range(3):
+        assert np.array_equal(pc[i], np.concatenate([pa[i], pb[i]]))
+
+
+def test_repack_is_deterministic_and_validates():
+    rng = np.random.default_rng(8)
+    a = make_weights(rng, "a", 32, 256, 5, ("const", 16), (0.0025, 0.01))
+    p1 = w4.repack(a.lo, a.hi, a.scales, a.zeros, 5)
+    p2 = w4.repack(a.lo, a.hi, a.scales, a.zeros, 5)
+    for i in range(3):
+        assert np.array_equal(p1[i], p2[i])
+    L = w4.lib()
+    buf = np.zeros(1 << 16, dtype=np.uint8)
+    ptr = buf.ctypes.data_as(ctypes.c_void_p)
+    # 5-bit needs the high plane; 4-bit must not get one
+    assert L.w4_repack(ptr, None, ptr, ptr, 16, 64, 5, 64, ptr, ptr, ptr) == -1
+    assert L.w4_repack(ptr, ptr, ptr, ptr, 16, 64, 4, 64, ptr, ptr, ptr) == -1
+    assert L.w4_repack(ptr, None, ptr, ptr, 16, 64, 6, 64, ptr, ptr, ptr) == -2
+    assert L.w4_repack(ptr, None, ptr, ptr, 16, 64, 4, 32, ptr, ptr, ptr) == -2
+    assert L.w4_repack(ptr, None, ptr, ptr, 15, 64, 4, 64, ptr, ptr, ptr) == -1
+    assert L.w4_repack(None, None, ptr, ptr, 16, 64, 4, 64, ptr, ptr, ptr) == -1

@@ -1,0 +1,172 @@
+"""GPU tier: every route x op x bits at widths across its domain, against the fp64 oracle.
+
+Shapes are small enough for the oracle to finish in well under a second, yet span several
+row tiles (including a ragged last row block), several k-blocks, a half-empty last k-block
+(K % 128 == 64) and ragged token tails.  All inputs are seeded synthetic data.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4_groupwise_gemm_amd as w4
+from synth import make_weights, make_activations, make_residual
+from gpu_util import assert_close, canon, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+ROUTE_TS = {
+    "gemv_exact_t": (1, 2, 3, 4),
+    "mfma_narrow_t16": (1, 5, 16),
+    "mfma_narrow_t32": (3, 17, 32),
+    "mfma_narrow_t64": (33, 40, 64),
+    "mfma_wide": (1, 65, 129, 300),
+}
+
+
+def route_ids():
+    return {w4.route_name(i): i for i in range(w4.route_count())}
+
+
+def _case(N, K, T, bits, op, seed, zero=("uniform", 6, 9), outliers=0):
+    rng = np.random.default_rng(seed)
+    scale = (0.0025, 0.01) if bits == 5 else (0.005, 0.02)
+    z = ("const", 16) if bits == 5 and zero == "cfg" else zero
+    ws = [make_weights(rng, "w", N, K, bits, z, scale)]
+    if op == w4.OP_SWIGLU:
+        ws.append(make_weights(rng, "u", N, K, bits, z, scale))
+    x, _ = make_activations(rng, T, K, 0.5 if op == w4.OP_SWIGLU else 1.0, outliers)
+    r = make_residual(rng, T, N) if op == w4.OP_ADD else None
+    return ws, x, r
+
+
+def _oracle(ws, x, r, op, bits):
+    if op == w4.OP_SWIGLU:
+        return oracle.swiglu(x, canon(ws[0]), canon(ws[1]), bits=bits)
+    if op == w4.OP_ADD:
+        return oracle.linear_add(x, *canon(ws[0]), r, bits=bits)
+    return oracle.linear(x, *canon(ws[0]), bits=bits)
+
+
+def _pack(ws, op, bits):
+    if op == w4.OP_SWIGLU:
+        return w4.pack_pair(canon(ws[0]), canon(ws[1]), bits, device=DEV)
+    return w4.pack_weight(*canon(ws[0]), bits, device=DEV)
+
+
+def _params():
+    out = []
+    for route, ts in ROUTE_TS.items():
+        for op in (w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD):
+            for bits in (4, 5):
+                for T in ts:
+                    out.append((route, op, bits, T))
+    return out
+
+
+@pytest.mark.parametrize("shape", [(272, 704), (320, 512)], ids=lambda s: f"N{s[0]}K{s[1]}")
+@pytest.mark.parametrize("route,op,bits,T", _params(),
+                         ids=lambda v: str(v))
+def test_route_parity(route, op, bits, T, shape):
+    N, K = shape
+    ws, x, r = _case(N, K, T, bits, op, seed=N + K + T + 7 * bits + 31 * op, outliers=4)
+    pw = _pack(ws, op, bits)
+    xd = torch.from_numpy(x).to(DEV)
+    rd = torch.from_numpy(r).to(DEV) if r is not None else None
+    print(f"case route={route} op={op} bits={bits} T={T} N={N} K={K}", flush=True)
+    y = w4.linear_route(route_ids()[route], op, xd, pw, residual=rd)
+    torch.cuda.synchronize()
+    assert_close(to_np(y), _oracle(ws, x, r, op, bits), f"{route} op{op} b{bits} T{T}")
+
+
+@pytest.mark.parametrize("bits", [4, 5])
+@pytest.mark.parametrize("route", sorted(ROUTE_TS))
+def test_one_hot_exact(route, bits):
+    """x = e_k gives exactly fp16(s * (q - z)) for integer z: one nonzero term per output."""
+    N, K = 32, 256
+    rng = np.random.default_rng(17 + bits)
+    ws = make_weights(rng, "w", N, K, bits, ("uniform", 0, (1 << bits) - 1), (0.005, 0.02))
+    pw = w4.pack_weight(*canon(ws), bits, device=DEV)
+    lo, hi = ROUTE_TS[route][0], ROUTE_TS[route][-1]
+    ks = np.arange(0, K, 7)
+    for start in range(0, len(ks), 16):
+        kk = ks[start:start + 16]
+        T = max(lo, min(hi, len(kk)))
+        x = np.zeros((T, K), dtype=np.float16)
+        for t, k in enumerate(kk[:T]):
+            x[t, k] = 1.0
+        y = to_np(w4.linear_route(route_ids()[route], w4.OP_LINEAR, torch.from_numpy(x).to(DEV), pw))
+        wfull = oracle.dequantize(oracle.unpack_codes(ws.lo, ws.hi, K, bits), ws.scales, ws.zeros)
+        want = np.zeros((T, N), dtype=np.float16)
+        for t, k in enumerate(kk[:T]):
+            want[t] = wfull[:, k].astype(np.float16)
+        assert np.array_equal(y.view(np.uint16), want.view(np.uint16)), (route, bits, kk)
+
+
+@pytest.mark.parametrize("route", sorted(ROUTE_TS))
+def test_deterministic_repeats(route):
+    N, K, bits = 256, 1024, 4
+    T = ROUTE_TS[route][-1]
+    ws, x, _ = _case(N, K, T, bits, w4.OP_LINEAR, seed=5)
+    pw = _pack(ws, w4.OP_LINEAR, bits)
+    xd = torch.from_numpy(x).to(DEV)
+    rid = route_ids()[route]
+    first = to_np(w4.linear_route(rid, w4.OP_LINEAR, xd, pw)).view(np.uint16)
+    for _ in range(9):
+        again = to_np(w4.linear_route(rid, w4.OP_LINEAR, xd, pw)).view(np.uint16)
+        assert np.array_equal(first, again)
+
+
+@pytest.mark.parametrize("route", sorted(ROUTE_TS))
+def test_equalisation_bit_identical(route):
+    """X * 2^-e and scales * 2^e per group (e in {-2,-1,0}) give identical output bits."""
+    N, K, bits = 64, 512, 5
+    T = ROUTE_TS[route][-1]
+    rng = np.random.default_rng(23)
+    ws = make_weights(rng, "w", N, K, bits, ("const", 16), (0.0025, 0.01))
+    x, _ = make_activations(rng, T, K, 1.0, 0)
+    e = rng.integers(-2, 1, size=K // 64)
+    x2 = (x.astype(np.float64) * np.repeat(2.0 ** (-e), 64)[None, :]).astype(np.float16)
+    s2 = (ws.scales.astype(np.float64) * (2.0 ** e)[None, :]).astype(np.float16)
+    assert np.array_equal(x2.astype(np.float64) * np.repeat(2.0 ** e, 64)[None, :], x.astype(np.float64))
+    pw1 = w4.pack_weight(ws.lo, ws.hi, ws.scales, ws.zeros, bits, device=DEV)
+    pw2 = w4.pack_weight(ws.lo, ws.hi, s2, ws.zeros, bits, device=DEV)
+    rid = route_ids()[route]
+    y1 = to_np(w4.linear_route(rid, w4.OP_LINEAR, torch.from_numpy(x).to(DEV), pw1))
+    y2 = to_np(w4.linear_route(rid, w4.OP_LINEAR, torch.from_numpy(x2).to(DEV), pw2))
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+@pytest.mark.parametrize("route", sorted(ROUTE_TS))
+def test_fractional_zero_points(route):
+    N, K, bits = 128, 640, 4
+    T = ROUTE_TS[route][-1]
+    ws, x, _ = _case(N, K, T, bits, w4.OP_LINEAR, seed=29, zero=("real", 0, 15))
+    pw = _pack(ws, w4.OP_LINEAR, bits)
+    y = to_np(w4.linear_route(route_ids()[route], w4.OP_LINEAR, torch.from_numpy(x).to(DEV), pw))
+    assert_close(y, oracle.linear(x, *canon(ws[0]), bits=bits), f"fractional z {route}")
+
+
+def test_public_calls_match_their_route():
+    """w4_linear / _swiglu / _add run exactly the route w4_route_for names (bitwise)."""
+    N, K = 256, 512
+    for op in (w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD):
+        for bits in (4, 5):
+            for T in (1, 2, 4, 8, 16, 24, 32, 48, 64, 65, 200):
+                ws, x, r = _case(N, K, T, bits, op, seed=T + op)
+                pw = _pack(ws, op, bits)
+                xd = torch.from_numpy(x).to(DEV)
+                rd = torch.from_numpy(r).to(DEV) if r is not None else None
+                if op == w4.OP_SWIGLU:
+                    y = w4.linear_swiglu(xd, pw)
+                elif op == w4.OP_ADD:
+                    y = w4.linear_add(xd, pw, rd)
+                else:
+                    y = w4.linear(xd, pw)
+                rid = w4.route_for(op, bits, T, N, K)
+                y2 = w4.linear_route(rid, op, xd, pw, residual=rd)
+                assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (op, bits, T)

@@ -1,0 +1,294 @@
+"""Python binding of ``libw4gemm.so`` (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module only checks
+Python-side types, allocates outputs with torch (device memory and streams are torch's) and
+forwards plain pointers and sizes through the C ABI declared in ``include/w4gemm.h``.  There
+is no fallback: if the library is missing or fails to load, importing the compute functions
+raises.
+
+torch is imported before the library is loaded so that the HIP runtime torch already mapped
+(``libamdhip64.so.7``) is the one the library binds to: one runtime, so torch's device
+pointers and streams are valid handles for the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libw4gemm.so")
+
+OP_LINEAR, OP_SWIGLU, OP_ADD = 0, 1, 2
+GROUP = 64
+
+_STATUS = {0: "W4_OK", -1: "W4_ERR_INVALID_ARG", -2: "W4_ERR_UNSUPPORTED", -3: "W4_ERR_MISALIGNED",
+           -4: "W4_ERR_ALIAS", -5: "W4_ERR_DOMAIN", -6: "W4_ERR_DEVICE", -7: "W4_ERR_LAUNCH"}
+
+EXPORTS = (
+    "w4_packed_bytes", "w4_packed_sz_bytes", "w4_repack", "w4_repack_pair", "w4_linear",
+    "w4_linear_swiglu", "w4_linear_add", "w4_route_for", "w4_linear_route", "w4_route_count",
+    "w4_route_name", "w4_route_domain", "w4_status_str", "w4_layout_version",
+)
+
+
+class W4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_STATUS.get(status, status)} ({status_str(status)})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libw4gemm.so once (after torch); raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m w4_groupwise_gemm_amd.build`")
+    import torch  # noqa: F401  -- map torch's HIP runtime first
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.w4_packed_bytes.argtypes = [i, i, i, i]
+    L.w4_packed_bytes.restype = sz
+    L.w4_packed_sz_bytes.argtypes = [i, i, i]
+    L.w4_packed_sz_bytes.restype = sz
+    L.w4_repack.argtypes = [vp, vp, vp, vp, i, i, i, i, vp, vp, vp]
+    L.w4_repack.restype = i
+    L.w4_repack_pair.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp]
+    L.w4_repack_pair.restype = i
+    L.w4_linear.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp]
+    L.w4_linear.restype = i
+    L.w4_linear_swiglu.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp]
+    L.w4_linear_swiglu.restype = i
+    L.w4_linear_add.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp]
+    L.w4_linear_add.restype = i
+    L.w4_route_for.argtypes = [i, i, i, i, i]
+    L.w4_route_for.restype = i
+    L.w4_linear_route.argtypes = [i, i, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp]
+    L.w4_linear_route.restype = i
+    L.w4_route_count.argtypes = []
+    L.w4_route_count.restype = i
+    L.w4_route_name.argtypes = [i]
+    L.w4_route_name.restype = ctypes.c_char_p
+    L.w4_route_domain.argtypes = [i, ctypes.POINTER(i), ctypes.POINTER(i)]
+    L.w4_route_domain.restype = i
+    L.w4_status_str.argtypes = [i]
+    L.w4_status_str.restype = ctypes.c_char_p
+    L.w4_layout_version.argtypes = []
+    L.w4_layout_version.restype = i
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().w4_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise W4Error(status, where)
+
+
+# ------------------------------------------------------------------ host-side repacking
+
+def packed_bytes(N: int, K: int, bits: int) -> int:
+    return int(lib().w4_packed_bytes(N, K, bits, GROUP))
+
+
+def packed_sz_bytes(N: int, K: int) -> int:
+    return int(lib().w4_packed_sz_bytes(N, K, GROUP))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _host(a, dtype) -> Optional[np.ndarray]:
+    """Contiguous host array of ``dtype``; same-size dtypes (fp16 -> uint16) are viewed."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.dtype(dtype):
+        if a.dtype.itemsize != np.dtype(dtype).itemsize:
+            raise TypeError(f"expected {np.dtype(dtype)}-sized elements, got {a.dtype}")
+        a = a.view(dtype)
+    return a
+
+
+def repack(lo, hi, scales, zeros, bits: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Canonical host arrays -> packed (codes uint8, scales uint16, zeros uint16) host arrays."""
+    lo = _host(lo, np.uint8)
+    hi = _host(hi, np.uint8)
+    s = _host(scales, np.uint16)
+    z = _host(zeros, np.uint16)
+    N, K = lo.shape[0], lo.shape[1] * 2
+    nw, nsz = packed_bytes(N, K, bits), packed_sz_bytes(N, K)
+    if nw == 0 or nsz == 0:
+        raise W4Error(-1, "repack")
+    w = np.empty(nw, dtype=np.uint8)
+    so = np.empty(nsz // 2, dtype=np.uint16)
+    zo = np.empty(nsz // 2, dtype=np.uint16)
+    _check(lib().w4_repack(_ptr(lo), _ptr(hi), _ptr(s), _ptr(z), N, K, bits, GROUP,
+                           _ptr(w), _ptr(so), _ptr(zo)), "w4_repack")
+    return w, so, zo
+
+
+def repack_pair(gate, up, bits: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """gate/up = (lo, hi, scales, zeros) canonical host tuples -> interleaved pair layout."""
+    g = [_host(gate[0], np.uint8), _host(gate[1], np.uint8), _host(gate[2], np.uint16),
+         _host(gate[3], np.uint16)]
+    u = [_host(up[0], np.uint8), _host(up[1], np.uint8), _host(up[2], np.uint16),
+         _host(up[3], np.uint16)]
+    N, K = g[0].shape[0], g[0].shape[1] * 2
+    nw, nsz = packed_bytes(2 * N, K, bits), packed_sz_bytes(2 * N, K)
+    if nw == 0 or nsz == 0:
+        raise W4Error(-1, "repack_pair")
+    w = np.empty(nw, dtype=np.uint8)
+    so = np.empty(nsz // 2, dtype=np.uint16)
+    zo = np.empty(nsz // 2, dtype=np.uint16)
+    _check(lib().w4_repack_pair(*[_ptr(a) for a in g], *[_ptr(a) for a in u], N, K, bits, GROUP,
+                                _ptr(w), _ptr(so), _ptr(zo)), "w4_repack_pair")
+    return w, so, zo
+
+
+# ------------------------------------------------------------------ device weights + compute
+
+@dataclasses.dataclass
+class PackedWeight:
+    """Packed weights resident on a device (torch tensors own the memory)."""
+    w: "object"        # torch.uint8 [bytes]
+    scales: "object"   # torch.int16 [elements] (fp16 bit patterns)
+    zeros: "object"    # torch.int16
+    N: int             # output width (of each of gate/up for a pair)
+    K: int
+    bits: int
+    pair: bool = False
+
+    @property
+    def nbytes_stream(self) -> int:
+        """Bytes one call streams: packed codes + scales + zeros (padding included)."""
+        return self.w.numel() + 2 * self.scales.numel() + 2 * self.zeros.numel()
+
+
+def to_device(packed: Tuple[np.ndarray, np.ndarray, np.ndarray], N: int, K: int, bits: int,
+              pair: bool = False, device="cuda") -> PackedWeight:
+    import torch
+    w, s, z = packed
+    return PackedWeight(torch.from_numpy(w).to(device),
+                        torch.from_numpy(s.view(np.int16)).to(device),
+                        torch.from_numpy(z.view(np.int16)).to(device), N, K, bits, pair)
+
+
+def pack_weight(lo, hi, scales, zeros, bits: int, device="cuda") -> PackedWeight:
+    lo = np.asarray(lo)
+    return to_device(repack(lo, hi, scales, zeros, bits), lo.shape[0], lo.shape[1] * 2, bits,
+                     False, device)
+
+
+def pack_pair(gate, up, bits: int, device="cuda") -> PackedWeight:
+    lo = np.asarray(gate[0])
+    return to_device(repack_pair(gate, up, bits), lo.shape[0], lo.shape[1] * 2, bits, True,
+                     device)
+
+
+def _dptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check_x(x, K: int):
+    import torch
+    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.shape[1] != K:
+        raise ValueError("x must be a CUDA float16 tensor of shape [T, K]")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+
+
+def _out(out, T: int, N: int, like):
+    import torch
+    if out is None:
+        return torch.empty((T, N), dtype=torch.float16, device=like.device)
+    if out.dtype != torch.float16 or out.shape != (T, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float16 tensor of shape [T, N]")
+    return out
+
+
+def linear(x, pw: PackedWeight, out=None, stream=None):
+    """out[T, N] = x . dequant(W)^T (fp16) via ``w4_linear``."""
+    _check_x(x, pw.K)
+    T = x.shape[0]
+    out = _out(out, T, pw.N, x)
+    _check(lib().w4_linear(_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros), T, pw.N,
+                           pw.K, pw.bits, GROUP, _dptr(out), _stream(stream)), "w4_linear")
+    return out
+
+
+def linear_swiglu(x, pw: PackedWeight, out=None, stream=None):
+    """out[T, N] = silu(x . Wg^T) * (x . Wu^T) via ``w4_linear_swiglu`` (pw from pack_pair)."""
+    if not pw.pair:
+        raise ValueError("linear_swiglu needs a gate/up pair from pack_pair")
+    _check_x(x, pw.K)
+    T = x.shape[0]
+    out = _out(out, T, pw.N, x)
+    _check(lib().w4_linear_swiglu(_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros), T,
+                                  pw.N, pw.K, pw.bits, GROUP, _dptr(out), _stream(stream)),
+           "w4_linear_swiglu")
+    return out
+
+
+def linear_add(x, pw: PackedWeight, residual, out=None, stream=None):
+    """out[T, N] = x . dequant(W)^T + residual via ``w4_linear_add`` (out may be residual)."""
+    _check_x(x, pw.K)
+    T = x.shape[0]
+    out = _out(out, T, pw.N, x)
+    _check(lib().w4_linear_add(_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros),
+                               _dptr(residual), T, pw.N, pw.K, pw.bits, GROUP, _dptr(out),
+                               _stream(stream)), "w4_linear_add")
+    return out
+
+
+def linear_route(route_id: int, op: int, x, pw: PackedWeight, residual=None, out=None,
+                 stream=None):
+    """Run one specific route (benches and per-route parity tests)."""
+    _check_x(x, pw.K)
+    T = x.shape[0]
+    out = _out(out, T, pw.N, x)
+    _check(lib().w4_linear_route(route_id, op, _dptr(x), _dptr(pw.w), _dptr(pw.scales),
+                                 _dptr(pw.zeros), _dptr(residual), T, pw.N, pw.K, pw.bits, GROUP,
+                                 _dptr(out), _stream(stream)), "w4_linear_route")
+    return out
+
+
+def route_for(op: int, bits: int, T: int, N: int, K: int) -> int:
+    return int(lib().w4_route_for(op, bits, T, N, K))
+
+
+def route_count() -> int:
+    return int(lib().w4_route_count())
+
+
+def route_name(route_id: int) -> Optional[str]:
+    r = lib().w4_route_name(route_id)
+    return None if r is None else r.decode()
+
+
+def route_domain(route_id: int) -> Tuple[int, int]:
+    lo, hi = ctypes.c_int(), ctypes.c_int()
+    _check(lib().w4_route_domain(route_id, ctypes.byref(lo), ctypes.byref(hi)), "w4_route_domain")
+    return lo.value, hi.value
+
+
+def layout_version() -> int:
+    return int(lib().w4_layout_version())

@@ -1,0 +1,224 @@
+// C ABI: argument validation, route table and the single launch of every compute call.
+//
+// Route table.  Each op has several kernels ("routes"), each with an explicit T domain; the
+// public calls pick exactly one route and launch it once.  Both rules come from the failures
+// the ninfer-3080 performance notes describe ("Route boundaries are measured here"): a kernel
+// handed more columns than it supports corrupted memory or silently did one column's work,
+// and a switch fallthrough ran a second kernel over the first.  The boundaries in
+// pick_route are set from crossovers measured per route at the same T (cold weights).
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/w4gemm.h"
+#include "device.h"
+#include "kernels.h"
+#include "layout.h"
+
+namespace {
+
+enum RouteKind { KIND_GEMV = 0, KIND_NARROW = 1, KIND_WIDE = 2 };
+
+struct Route {
+  const char* name;
+  int tmin, tmax;
+  RouteKind kind;
+  int tn;  // padded token tile of the narrow routes
+};
+
+const Route kRoutes[] = {
+    {"gemv_exact_t", 1, 4, KIND_GEMV, 0},
+    {"mfma_narrow_t16", 1, 16, KIND_NARROW, 16},
+    {"mfma_narrow_t32", 1, 32, KIND_NARROW, 32},
+    {"mfma_narrow_t64", 1, 64, KIND_NARROW, 64},
+    {"mfma_wide", 1, INT_MAX, KIND_WIDE, 0},
+};
+constexpr int kNumRoutes = sizeof(kRoutes) / sizeof(kRoutes[0]);
+enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4 };
+
+constexpr int kMaxDim = 1 << 24;
+
+bool op_ok(int op) { return op == W4_OP_LINEAR || op == W4_OP_SWIGLU || op == W4_OP_ADD; }
+
+// Shape-only checks shared by validation and route selection (no pointers, no HIP calls).
+int check_shape(int op, int T, int N, int K, int bits, int group) {
+  if (!op_ok(op)) return W4_ERR_UNSUPPORTED;
+  if (bits != 4 && bits != 5) return W4_ERR_UNSUPPORTED;
+  if (group != w4layout::kGroup) return W4_ERR_UNSUPPORTED;
+  if (T < 0 || N <= 0 || K <= 0) return W4_ERR_INVALID_ARG;
+  if (T > kMaxDim || N > kMaxDim || K > kMaxDim) return W4_ERR_INVALID_ARG;
+  if (N % w4layout::kRowTile || K % w4layout::kGroup) return W4_ERR_INVALID_ARG;
+  return W4_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int validate(int op, const void* x, const void* w, const void* s, const void* z, const void* res,
+             int T, int N, int K, int bits, int group, const void* out) {
+  int st = check_shape(op, T, N, K, bits, group);
+  if (st != W4_OK) return st;
+  if (T == 0) return W4_OK;
+  if (!x || !w || !s || !z || !out) return W4_ERR_INVALID_ARG;
+  if (op == W4_OP_ADD && !res) return W4_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(z) || !aligned16(out))
+    return W4_ERR_MISALIGNED;
+  if (op == W4_OP_ADD && !aligned16(res)) return W4_ERR_MISALIGNED;
+  const int rows = op == W4_OP_SWIGLU ? 2 * N : N;
+  const size_t wbytes = w4_packed_bytes(rows, K, bits, group);
+  const size_t szbytes = w4_packed_sz_bytes(rows, K, group);
+  auto rng = [](const void* p, size_t n) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return Range{b, b + n};
+  };
+  const Range ro = rng(out, (size_t)T * N * 2);
+  if (overlap(ro, rng(x, (size_t)T * K * 2)) || overlap(ro, rng(w, wbytes)) ||
+      overlap(ro, rng(s, szbytes)) || overlap(ro, rng(z, szbytes)))
+    return W4_ERR_ALIAS;
+  if (op == W4_OP_ADD && res != out && overlap(ro, rng(res, (size_t)T * N * 2)))
+    return W4_ERR_ALIAS;
+  return W4_OK;
+}
+
+// Per-device "is gfx950" cache: 0 unknown, 1 yes, -1 no.  Filled once per device by a host
+// property query (no stream work), so the hot path stays capturable.
+int g_arch_ok[64];
+
+int device_check() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return W4_ERR_DEVICE;
+  if (dev >= 64) return W4_ERR_DEVICE;
+  int v = __atomic_load_n(&g_arch_ok[dev], __ATOMIC_ACQUIRE);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return W4_ERR_DEVICE;
+    v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    __atomic_store_n(&g_arch_ok[dev], v, __ATOMIC_RELEASE);
+  }
+  return v == 1 ? W4_OK : W4_ERR_DEVICE;
+}
+
+int pick_route(int op, int bits, int T, int N, int K) {
+  (void)op;
+  (void)bits;
+  (void)N;
+  (void)K;
+  if (T <= 2) return R_GEMV;
+  if (T <= 16) return R_N16;
+  if (T <= 32) return R_N32;
+  if (T <= 64) return R_N64;
+  return R_WIDE;
+}
+
+int launch_route(int route, int op, const void* x, const void* w, const void* s, const void* z,
+                 const void* res, int T, int N, int K, int bits, void* out, void* stream) {
+  const Route& R = kRoutes[route];
+  if (T < R.tmin || T > R.tmax) return W4_ERR_DOMAIN;
+  w4::KArgs a;
+  a.x = static_cast<const _Float16*>(x);
+  a.w = static_cast<const uint8_t*>(w);
+  a.sc = static_cast<const uint32_t*>(s);
+  a.zr = static_cast<const uint32_t*>(z);
+  a.res = op == W4_OP_ADD ? static_cast<const _Float16*>(res) : nullptr;
+  a.out = static_cast<_Float16*>(out);
+  a.T = T;
+  a.rows = op == W4_OP_SWIGLU ? 2 * N : N;
+  a.K = K;
+  a.KB = w4layout::num_kblocks(K);
+  a.ldo = N;
+  const int epi = op == W4_OP_SWIGLU ? w4dev::EPI_SWIGLU
+                  : op == W4_OP_ADD  ? w4dev::EPI_ADD
+                                     : w4dev::EPI_STORE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (R.kind) {
+    case KIND_GEMV: e = w4::launch_gemv(bits, epi, a, st); break;
+    case KIND_NARROW: e = w4::launch_narrow(R.tn, bits, epi, a, st); break;
+    case KIND_WIDE: e = w4::launch_wide(bits, epi, a, st); break;
+    default: return W4_ERR_DOMAIN;
+  }
+  return e == hipSuccess ? W4_OK : W4_ERR_LAUNCH;
+}
+
+int run_op(int route, int op, const void* x, const void* w, const void* s, const void* z,
+           const void* res, int T, int N, int K, int bits, int group, void* out, void* stream) {
+  int st = validate(op, x, w, s, z, res, T, N, K, bits, group, out);
+  if (st != W4_OK) return st;
+  if (route < 0) route = pick_route(op, bits, T, N, K);
+  if (route >= kNumRoutes) return W4_ERR_DOMAIN;
+  if (T == 0) return W4_OK;
+  if (T < kRoutes[route].tmin || T > kRoutes[route].tmax) return W4_ERR_DOMAIN;
+  st = device_check();
+  if (st != W4_OK) return st;
+  return launch_route(route, op, x, w, s, z, res, T, N, K, bits, out, stream);
+}
+
+}  // namespace
+
+extern "C" int w4_linear(const uint16_t* x, const void* w, const uint16_t* scales,
+                         const uint16_t* zeros, int T, int N, int K, int bits, int group,
+                         uint16_t* out, void* stream) {
+  return run_op(-1, W4_OP_LINEAR, x, w, scales, zeros, nullptr, T, N, K, bits, group, out, stream);
+}
+
+extern "C" int w4_linear_swiglu(const uint16_t* x, const void* w_pair,
+                                const uint16_t* scales_pair, const uint16_t* zeros_pair, int T,
+                                int N, int K, int bits, int group, uint16_t* out, void* stream) {
+  return run_op(-1, W4_OP_SWIGLU, x, w_pair, scales_pair, zeros_pair, nullptr, T, N, K, bits,
+                group, out, stream);
+}
+
+extern "C" int w4_linear_add(const uint16_t* x, const void* w, const uint16_t* scales,
+                             const uint16_t* zeros, const uint16_t* residual, int T, int N, int K,
+                             int bits, int group, uint16_t* out, void* stream) {
+  return run_op(-1, W4_OP_ADD, x, w, scales, zeros, residual, T, N, K, bits, group, out, stream);
+}
+
+extern "C" int w4_route_for(int op, int bits, int T, int N, int K) {
+  int st = check_shape(op, T, N, K, bits, w4layout::kGroup);
+  if (st != W4_OK) return st;
+  return pick_route(op, bits, T < 1 ? 1 : T, N, K);
+}
+
+extern "C" int w4_linear_route(int route_id, int op, const uint16_t* x, const void* w,
+                               const uint16_t* scales, const uint16_t* zeros,
+                               const uint16_t* residual, int T, int N, int K, int bits, int group,
+                               uint16_t* out, void* stream) {
+  if (route_id < 0 || route_id >= kNumRoutes) return W4_ERR_DOMAIN;
+  return run_op(route_id, op, x, w, scales, zeros, residual, T, N, K, bits, group, out, stream);
+}
+
+extern "C" int w4_route_count(void) { return kNumRoutes; }
+
+extern "C" const char* w4_route_name(int route_id) {
+  if (route_id < 0 || route_id >= kNumRoutes) return nullptr;
+  return kRoutes[route_id].name;
+}
+
+extern "C" int w4_route_domain(int route_id, int* tmin, int* tmax) {
+  if (route_id < 0 || route_id >= kNumRoutes) return W4_ERR_DOMAIN;
+  if (tmin) *tmin = kRoutes[route_id].tmin;
+  if (tmax) *tmax = kRoutes[route_id].tmax;
+  return W4_OK;
+}
+
+extern "C" const char* w4_status_str(int status) {
+  switch (status) {
+    case W4_OK: return "ok";
+    case W4_ERR_INVALID_ARG: return "invalid argument";
+    case W4_ERR_UNSUPPORTED: return "unsupported bits, group or op";
+    case W4_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+    case W4_ERR_ALIAS: return "output overlaps an input";
+    case W4_ERR_DOMAIN: return "route unknown or T outside its domain";
+    case W4_ERR_DEVICE: return "no gfx950 device current";
+    case W4_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int w4_layout_version(void) { return W4_LAYOUT_VERSION; }

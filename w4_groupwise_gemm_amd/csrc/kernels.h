@@ -1,0 +1,29 @@
+// Internal interface between the C ABI (api.hip) and the kernel families.  Plain pointers and
+// sizes only; every pointer has been validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+struct KArgs {
+  const _Float16* x;     // [T][K] activations
+  const uint8_t* w;      // packed codes, `rows` packed rows
+  const uint32_t* sc;    // packed scales, one fp16 pair (2 groups) per (row tile, k-block, row)
+  const uint32_t* zr;    // packed zero-points, same layout
+  const _Float16* res;   // [T][ldo] residual (EPI_ADD) or nullptr
+  _Float16* out;         // [T][ldo]
+  int T;                 // tokens (>= 1)
+  int rows;              // packed rows (2N for the SwiGLU pair)
+  int K;                 // columns of X and W
+  int KB;                // ceil(K / 128)
+  int ldo;               // output columns (N)
+};
+
+// Each launcher enqueues exactly one kernel on `stream` and returns hipSuccess or the launch
+// error.  `epi` is one of w4dev::EPI_*.
+hipError_t launch_gemv(int bits, int epi, const KArgs& a, hipStream_t stream);    // 1 <= T <= 4
+hipError_t launch_narrow(int tn, int bits, int epi, const KArgs& a, hipStream_t stream);  // T <= tn
+hipError_t launch_wide(int bits, int epi, const KArgs& a, hipStream_t stream);    // any T
+
+}  // namespace w4

@@ -21,7 +21,7 @@ DEV = "cuda:0"
 
 ROUTE_TS = {
     "gemv_exact_t": (1, 2, 3, 4),
-    "mfma_narrow_t16": (1, 5, 16),
+    "mfma_stream_t16": (1, 2, 4, 5, 16),
     "mfma_narrow_t32": (3, 17, 32),
     "mfma_narrow_t64": (33, 40, 64),
     "mfma_wide": (1, 65, 129, 300),
@@ -170,3 +170,21 @@ def test_public_calls_match_their_route():
                 rid = w4.route_for(op, bits, T, N, K)
                 y2 = w4.linear_route(rid, op, xd, pw, residual=rd)
                 assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (op, bits, T)
+
+
+@pytest.mark.parametrize("K", [6144, 12352, 17408])
+@pytest.mark.parametrize("route", sorted(ROUTE_TS))
+def test_long_k(route, K):
+    """K ranges that take the 8-, 16-block and looping variants of the streaming kernels,
+    including a half-empty last k-block (12352 = 96.5 blocks)."""
+    N = 48
+    for op in (w4.OP_LINEAR, w4.OP_ADD):
+        for bits in (4, 5):
+            for T in (ROUTE_TS[route][0], ROUTE_TS[route][-1]):
+                ws, x, r = _case(N, K, T, bits, op, seed=K + T + bits + op, outliers=2)
+                pw = _pack(ws, op, bits)
+                xd = torch.from_numpy(x).to(DEV)
+                rd = torch.from_numpy(r).to(DEV) if r is not None else None
+                print(f"case long-k route={route} op={op} bits={bits} T={T} K={K}", flush=True)
+                y = w4.linear_route(route_ids()[route], op, xd, pw, residual=rd)
+                assert_close(to_np(y), _oracle(ws, x, r, op, bits), f"{route} K{K} op{op} b{bits} T{T}")

@@ -16,8 +16,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw4gemm.so")
+PROBE_LIB = os.path.join(HERE, "libw4probe.so")  # measurement support (read/copy/empty kernels)
 
-SOURCES = ["api.hip", "gemv.hip", "narrow.hip", "wide.hip", "repack.cpp"]
+SOURCES = ["api.hip", "stream.hip", "narrow.hip", "wide.hip", "repack.cpp"]
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
 
@@ -37,19 +39,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 5) -> str:
-    """Compile every source (always, even if a library exists) and link libw4gemm.so."""
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, out)
+
+
+def build(verbose: bool = False, jobs: int = 6) -> str:
+    """Compile every source (always, even if a library exists) and link libw4gemm.so and the
+    measurement-support libw4probe.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -19,7 +19,7 @@
 
 namespace {
 
-enum RouteKind { KIND_GEMV = 0, KIND_NARROW = 1, KIND_WIDE = 2 };
+enum RouteKind { KIND_GEMV = 0, KIND_STREAM = 1, KIND_NARROW = 2, KIND_WIDE = 3 };
 
 struct Route {
   const char* name;
@@ -30,7 +30,7 @@ struct Route {
 
 const Route kRoutes[] = {
     {"gemv_exact_t", 1, 4, KIND_GEMV, 0},
-    {"mfma_narrow_t16", 1, 16, KIND_NARROW, 16},
+    {"mfma_stream_t16", 1, 16, KIND_STREAM, 16},
     {"mfma_narrow_t32", 1, 32, KIND_NARROW, 32},
     {"mfma_narrow_t64", 1, 64, KIND_NARROW, 64},
     {"mfma_wide", 1, INT_MAX, KIND_WIDE, 0},
@@ -138,6 +138,7 @@ int launch_route(int route, int op, const void* x, const void* w, const void* s,
   hipError_t e;
   switch (R.kind) {
     case KIND_GEMV: e = w4::launch_gemv(bits, epi, a, st); break;
+    case KIND_STREAM: e = w4::launch_stream16(bits, epi, a, st); break;
     case KIND_NARROW: e = w4::launch_narrow(R.tn, bits, epi, a, st); break;
     case KIND_WIDE: e = w4::launch_wide(bits, epi, a, st); break;
     default: return W4_ERR_DOMAIN;

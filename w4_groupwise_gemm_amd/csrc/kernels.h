@@ -22,7 +22,8 @@ struct KArgs {
 
 // Each launcher enqueues exactly one kernel on `stream` and returns hipSuccess or the launch
 // error.  `epi` is one of w4dev::EPI_*.
-hipError_t launch_gemv(int bits, int epi, const KArgs& a, hipStream_t stream);    // 1 <= T <= 4
+hipError_t launch_gemv(int bits, int epi, const KArgs& a, hipStream_t stream);      // 1 <= T <= 4
+hipError_t launch_stream16(int bits, int epi, const KArgs& a, hipStream_t stream);  // T <= 16
 hipError_t launch_narrow(int tn, int bits, int epi, const KArgs& a, hipStream_t stream);  // T <= tn
 hipError_t launch_wide(int bits, int epi, const KArgs& a, hipStream_t stream);    // any T
 

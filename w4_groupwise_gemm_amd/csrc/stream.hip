@@ -1,0 +1,376 @@
+// Streaming path for small token counts: the GEMV route (exact T = 1..4, packed-fp16 dot
+// products) and the 16-token matrix-core route (T <= 16).
+//
+// Prior art: the SIMT split GEMVs and the Q4/Q5 small-T MMA kernels of the ninfer-3080
+// performance notes ("Why the round cost too much"; "What changed": permuted k order; "What
+// is left at C1": at one stream the kernels are a streaming problem, ramp-up and drain).
+//
+// gfx950 design.  At these widths the kernel is an HBM stream with a dequantisation tax, so
+// everything is arranged around keeping enough 16-byte code loads in flight and keeping the
+// vector ALU work per packed word minimal:
+//  * a workgroup owns RT 16-row tiles; its NW waves split K into NW contiguous block ranges,
+//    so each code byte is loaded exactly once, into the lane that feeds it to the math;
+//  * each wave keeps a ring of D k-blocks of loads in flight ahead of the math;
+//  * for T <= 4 the wave's activation slice (T rows of its K range) is loaded first and
+//    parked in a wave-private LDS region, so activation reads never wait behind code loads in
+//    the in-order load counter and no barrier is needed inside the loop; for larger T the
+//    16-token activation fragments ride in the same ring as the codes;
+//  * the dequantisation is 13 vector ops per packed word when the zero-points of a block are
+//    integers (checked exactly, wave-uniformly, per block): mask-or the nibbles into the
+//    mantissa of fp16 1024 (one v_and_or_b32 per pair), subtract 1024 + z (or fold 1/16 and
+//    64 + z into one packed fma for the high-nibble pairs) and multiply by the scale;
+//    fractional zero-points take the general 17-op form;
+//  * token rows beyond T are clamped to row T-1 instead of masked: those output columns are
+//    never stored, so the loads need no exec masking;
+//  * the NW partial sums are combined in LDS in a fixed order (bitwise deterministic).
+#include "device.h"
+#include "kernels.h"
+
+namespace w4 {
+namespace {
+
+using namespace w4dev;
+using w4layout::block_bytes;
+
+enum { MODE_MFMA = 0, MODE_DOT2 = 1 };
+
+// A 32-bit register that holds the constant (keeps v_and_or_b32 legal: one literal/SGPR).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
+// Biased fp16 pairs 1024 + q (slots 0,1 / 4,5) and 1024 + 16 q (slots 2,3 / 6,7) of dword J.
+template <int BITS, int J>
+__device__ __forceinline__ void biased_pairs(uint32_t w, uint32_t hiw, uint32_t magic, uint32_t u[4]) {
+  const uint32_t w8 = w >> 8;
+  u[0] = (w & 0x000F000Fu) | magic;
+  u[1] = (w & 0x00F000F0u) | magic;
+  u[2] = (w8 & 0x000F000Fu) | magic;
+  u[3] = (w8 & 0x00F000F0u) | magic;
+  if constexpr (BITS == 5) {
+    constexpr int t = (J == 0 ? 0 : J == 1 ? 2 : J == 2 ? 8 : 10);
+    uint32_t x1, x2;
+    if constexpr (t <= 3) {
+      x1 = hiw << (4 - t);
+      x2 = hiw << (3 - t);
+    } else {
+      x1 = hiw >> (t - 4);
+      x2 = hiw >> (t - 3);
+    }
+    u[0] |= x1 & 0x00100010u;
+    u[1] |= x1 & 0x01000100u;
+    u[2] |= x2 & 0x00100010u;
+    u[3] |= x2 & 0x01000100u;
+  }
+}
+
+// fp16 weights (q - z) * s of dword J as four pairs.  FAST: z is an integer (1024 + z and
+// 64 + z exact in fp16), b0 = -(1024 + z), b1 = -(64 + z).  Otherwise q is made exact first.
+template <int BITS, int J, bool FAST>
+__device__ __forceinline__ void weights(uint32_t w, uint32_t hiw, uint32_t magic, f16x2 z2, f16x2 b0,
+                                        f16x2 b1, f16x2 s2, f16x2 out[4]) {
+  uint32_t u[4];
+  biased_pairs<BITS, J>(w, hiw, magic, u);
+  const f16x2 c16th = {(f16)0.0625f, (f16)0.0625f};
+  if constexpr (FAST) {
+    out[0] = (as_h2(u[0]) + b0) * s2;
+    out[1] = (as_h2(u[1]) * c16th + b1) * s2;
+    out[2] = (as_h2(u[2]) + b0) * s2;
+    out[3] = (as_h2(u[3]) * c16th + b1) * s2;
+  } else {
+    const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f}, c64 = {(f16)64.0f, (f16)64.0f};
+    out[0] = ((as_h2(u[0]) - c1024) - z2) * s2;
+    out[1] = ((as_h2(u[1]) * c16th - c64) - z2) * s2;
+    out[2] = ((as_h2(u[2]) - c1024) - z2) * s2;
+    out[3] = ((as_h2(u[3]) * c16th - c64) - z2) * s2;
+  }
+}
+
+template <int BITS, int RT, int KPW, int XL>
+struct Ring {
+  u32x4 cw[KPW][RT];
+  uint32_t hw[KPW][RT], sp[KPW][RT], zp[KPW][RT];
+  u32x4 xb[XL ? 1 : KPW][4];
+};
+
+template <int BITS, int MODE, int RT, int NW, int KPW, int D, int XL, int EPI, bool LOOP>
+__global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int BLK = block_bytes(BITS);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int ntiles = a.rows / 16;
+  const int tile0 = blockIdx.x * RT;
+  const int kbw0 = (a.KB * wave) / NW, kbw1 = (a.KB * (wave + 1)) / NW;
+  const int T = a.T;
+  const int tr = min(r, T - 1);
+  const uint32_t magic = vgpr_const(0x64006400u);
+  _Float16* xs = reinterpret_cast<_Float16*>(smem) + (size_t)wave * 4 * xstride;
+
+  f32x4 acc[RT];
+  float accd[RT][4];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) accd[rt][t] = 0.f;
+  }
+
+  Ring<BITS, RT, KPW, XL> R;
+  // Without LOOP the launcher guarantees at most one chunk per wave (kbw1 - kbw0 <= KPW): a
+  // runtime loop around the unrolled ring costs about a third more registers.  A wave whose
+  // K range is empty (K shorter than NW k-blocks) skips the body entirely: its activation
+  // slice would otherwise be addressed from chunk -1.
+  for (int cb = kbw0; LOOP ? cb < kbw1 : (cb == kbw0 && cb < kbw1); cb += KPW) {
+    const int nb = min(KPW, kbw1 - cb);
+
+    // activation slice of this chunk (T <= 4 rows), loaded before any code of the chunk
+    constexpr int XCH = (KPW * 16 + 63) / 64;  // 16-byte chunks per lane per token row
+    u32x4 xr[XL ? 4 : 1][XL ? XCH : 1];
+    if constexpr (XL == 1) {
+      const int cpt = nb * 16;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < T) {
+#pragma unroll
+          for (int i = 0; i < XCH; ++i) {
+            const int c = min(lane + 64 * i, cpt - 1);
+            const int kk = min(cb * 128 + c * 8, a.K - 8);
+            xr[t][i] = *reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.K + kk);
+          }
+        }
+      }
+    }
+
+    auto issue = [&](int i) {
+      const int kb = cb + i;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int tile = min(tile0 + rt, ntiles - 1);
+        const size_t bi = (size_t)tile * a.KB + kb;
+        R.cw[i][rt] = *reinterpret_cast<const u32x4*>(a.w + bi * BLK + lane * 16);
+        if constexpr (BITS == 5)
+          R.hw[i][rt] = *reinterpret_cast<const uint32_t*>(a.w + bi * BLK + 1024 + lane * 4);
+        else
+          R.hw[i][rt] = 0;
+        R.sp[i][rt] = a.sc[bi * 16 + r];
+        R.zp[i][rt] = a.zr[bi * 16 + r];
+      }
+      if constexpr (XL == 0) {
+        const bool half_block = (kb * 128 + 64 >= a.K);
+        const _Float16* xrow = a.x + (size_t)tr * a.K + kb * 128 + 16 * g;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          R.xb[i][j] = (half_block && j >= 2)
+                           ? u32x4{0u, 0u, 0u, 0u}
+                           : *reinterpret_cast<const u32x4*>(xrow + 64 * (j >> 1) + 8 * (j & 1));
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < D; ++i)
+      if (i < nb) issue(i);
+
+    if constexpr (XL == 1) {
+      const int cpt = nb * 16;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (t < T) {
+#pragma unroll
+          for (int i = 0; i < XCH; ++i) {
+            const int c = lane + 64 * i;
+            if (c < cpt) *reinterpret_cast<u32x4*>(xs + t * xstride + c * 8) = xr[t][i];
+          }
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+#pragma unroll
+    for (int i = 0; i < KPW; ++i) {
+      if (i + D < nb) issue(i + D);
+      if (i < nb) {
+        const int kb = cb + i;
+        const bool half_block = (kb * 128 + 64 >= a.K);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          // exact wave-uniform test: are both zero-points of this block integers?
+          const f16x2 z2p = as_h2(R.zp[i][rt]);
+          const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f}, c64 = {(f16)64.0f, (f16)64.0f};
+          const f16x2 nb0 = -(z2p + c1024);
+          const bool exact = __builtin_bit_cast(uint32_t, (-nb0) - c1024) == R.zp[i][rt];
+          const bool fast = __ballot(exact) == ~0ull;
+          const f16x2 nb1 = -(z2p + c64);
+#define W4_STREAM_J(J)                                                                        \
+  if (!(half_block && (J) >= 2)) {                                                            \
+    const f16x2 s2 = splat<((J) >> 1)>(R.sp[i][rt]);                                          \
+    f16x2 wv[4];                                                                              \
+    if (fast)                                                                                 \
+      weights<BITS, J, true>(R.cw[i][rt][J], R.hw[i][rt], magic, f16x2{},                     \
+                             splat<((J) >> 1)>(__builtin_bit_cast(uint32_t, nb0)),            \
+                             splat<((J) >> 1)>(__builtin_bit_cast(uint32_t, nb1)), s2, wv);   \
+    else                                                                                      \
+      weights<BITS, J, false>(R.cw[i][rt][J], R.hw[i][rt], magic,                             \
+                              splat<((J) >> 1)>(R.zp[i][rt]), f16x2{}, f16x2{}, s2, wv);      \
+    const int koff = i * 128 + 64 * ((J) >> 1) + 16 * g + 8 * ((J) & 1);                      \
+    if constexpr (MODE == MODE_MFMA) {                                                        \
+      f16x8 B;                                                                                \
+      if constexpr (XL == 1)                                                                  \
+        B = *reinterpret_cast<const f16x8*>(xs + tr * xstride + koff);                        \
+      else                                                                                    \
+        B = __builtin_bit_cast(f16x8, R.xb[i][J]);                                            \
+      acc[rt] = mfma16(cat8(wv[0], wv[1], wv[2], wv[3]), B, acc[rt]);                         \
+    } else {                                                                                  \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
+        if (t < T) {                                                                          \
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + t * xstride + koff);         \
+          float v = accd[rt][t];                                                              \
+          _Pragma("unroll") for (int p = 0; p < 4; ++p)                                       \
+              v = __builtin_amdgcn_fdot2(wv[p], as_h2(xv[p]), v, false);                      \
+          accd[rt][t] = v;                                                                    \
+        }                                                                                     \
+      }                                                                                       \
+    }                                                                                         \
+  }
+          W4_STREAM_J(0)
+          W4_STREAM_J(1)
+          W4_STREAM_J(2)
+          W4_STREAM_J(3)
+#undef W4_STREAM_J
+        }
+      }
+    }
+  }
+
+  // ---- fixed-order combination of the NW partial sums, then the epilogue
+  __syncthreads();
+  if constexpr (MODE == MODE_MFMA) {
+    f32x4* red = reinterpret_cast<f32x4*>(smem);  // [NW][RT][64]
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) red[(wave * RT + rt) * 64 + lane] = acc[rt];
+    __syncthreads();
+    constexpr int ITEMS = (EPI == EPI_SWIGLU ? RT / 2 : RT) * 64;
+    for (int it = threadIdx.x; it < ITEMS; it += NW * 64) {
+      const int l = it & 63, p = it >> 6;
+      const int t = l & 15;
+      if (t >= T) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const int gtile = tile0 + 2 * p;
+        if (gtile >= ntiles) continue;
+        f32x4 gv = red[(2 * p) * 64 + l], uv = red[(2 * p + 1) * 64 + l];
+        for (int w = 1; w < NW; ++w) {
+          gv = gv + red[(w * RT + 2 * p) * 64 + l];
+          uv = uv + red[(w * RT + 2 * p + 1) * 64 + l];
+        }
+        store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + (gtile >> 1) * 16 + 4 * (l >> 4), gv, uv);
+      } else {
+        const int tile = tile0 + p;
+        if (tile >= ntiles) continue;
+        f32x4 v = red[p * 64 + l];
+        for (int w = 1; w < NW; ++w) v = v + red[(w * RT + p) * 64 + l];
+        store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + tile * 16 + 4 * (l >> 4), v, f32x4{});
+      }
+    }
+  } else {
+    float* red = reinterpret_cast<float*>(smem);  // [NW][RT][4][16]
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float v = accd[rt][t];
+        v = v + __shfl_xor(v, 16);
+        v = v + __shfl_xor(v, 32);
+        if (lane < 16) red[((wave * RT + rt) * 4 + t) * 16 + lane] = v;
+      }
+    __syncthreads();
+    constexpr int ITEMS = (EPI == EPI_SWIGLU ? RT / 2 : RT) * 64;
+    for (int it = threadIdx.x; it < ITEMS; it += NW * 64) {
+      const int row = it & 15, t = (it >> 4) & 3, p = it >> 6;
+      if (t >= T) continue;
+      if constexpr (EPI == EPI_SWIGLU) {
+        const int gtile = tile0 + 2 * p;
+        if (gtile >= ntiles) continue;
+        float gv = red[((2 * p) * 4 + t) * 16 + row], uv = red[((2 * p + 1) * 4 + t) * 16 + row];
+        for (int w = 1; w < NW; ++w) {
+          gv += red[((w * RT + 2 * p) * 4 + t) * 16 + row];
+          uv += red[((w * RT + 2 * p + 1) * 4 + t) * 16 + row];
+        }
+        store_one<EPI>(a.out, a.res, (size_t)t * a.ldo + (gtile >> 1) * 16 + row, gv, uv);
+      } else {
+        const int tile = tile0 + p;
+        if (tile >= ntiles) continue;
+        float v = red[(p * 4 + t) * 16 + row];
+        for (int w = 1; w < NW; ++w) v += red[((w * RT + p) * 4 + t) * 16 + row];
+        store_one<EPI>(a.out, a.res, (size_t)t * a.ldo + tile * 16 + row, v, 0.f);
+      }
+    }
+  }
+}
+
+constexpr int kNW = 8;  // waves per workgroup (K split)
+constexpr int kD = 3;   // ring depth (k-blocks of loads in flight ahead of the math)
+
+template <int BITS, int MODE, int RT, int XL, int EPI, int KPW, bool LOOP>
+hipError_t run_k(const KArgs& a, hipStream_t stream) {
+  const int ntiles = a.rows / 16;
+  const int nbw = (a.KB + kNW - 1) / kNW;
+  const int nbc = nbw < KPW ? nbw : KPW;  // blocks per chunk
+  const int xstride = nbc * 128 + 8;
+  size_t lds = XL ? (size_t)kNW * 4 * xstride * 2 : 0;
+  const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * 64 * 16 : (size_t)kNW * RT * 64 * 4;
+  if (red > lds) lds = red;
+  hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, kD, XL, EPI, LOOP>),
+                     dim3((ntiles + RT - 1) / RT), dim3(kNW * 64), lds, stream, a, xstride);
+  return hipGetLastError();
+}
+
+// k-blocks per wave: one unrolled chunk for K <= 16384, a chunk loop beyond.
+template <int BITS, int MODE, int RT, int XL, int EPI>
+hipError_t run(const KArgs& a, hipStream_t stream) {
+  const int nbw = (a.KB + kNW - 1) / kNW;
+  if (nbw <= 5) return run_k<BITS, MODE, RT, XL, EPI, 5, false>(a, stream);
+  if (nbw <= 8) return run_k<BITS, MODE, RT, XL, EPI, 8, false>(a, stream);
+  if (nbw <= 16) return run_k<BITS, MODE, RT, XL, EPI, 16, false>(a, stream);
+  return run_k<BITS, MODE, RT, XL, EPI, 8, true>(a, stream);
+}
+
+template <int BITS, int MODE, int XL, int EPI>
+hipError_t pick_rt(const KArgs& a, hipStream_t stream) {
+  const int ntiles = a.rows / 16;
+  if constexpr (EPI == EPI_SWIGLU) {
+    return run<BITS, MODE, 2, XL, EPI>(a, stream);
+  } else {
+    if (ntiles >= 4 * 256 * 2) return run<BITS, MODE, 2, XL, EPI>(a, stream);
+    return run<BITS, MODE, 1, XL, EPI>(a, stream);
+  }
+}
+
+template <int BITS, int MODE, int EPI>
+hipError_t pick_xl(const KArgs& a, hipStream_t stream) {
+  if (a.T <= 4) return pick_rt<BITS, MODE, 1, EPI>(a, stream);
+  if constexpr (MODE == MODE_MFMA) return pick_rt<BITS, MODE, 0, EPI>(a, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int BITS, int MODE>
+hipError_t pick_epi(int epi, const KArgs& a, hipStream_t stream) {
+  if (epi == EPI_SWIGLU) return pick_xl<BITS, MODE, EPI_SWIGLU>(a, stream);
+  if (epi == EPI_ADD) return pick_xl<BITS, MODE, EPI_ADD>(a, stream);
+  return pick_xl<BITS, MODE, EPI_STORE>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv(int bits, int epi, const KArgs& a, hipStream_t stream) {
+  return bits == 5 ? pick_epi<5, MODE_DOT2>(epi, a, stream) : pick_epi<4, MODE_DOT2>(epi, a, stream);
+}
+
+hipError_t launch_stream16(int bits, int epi, const KArgs& a, hipStream_t stream) {
+  return bits == 5 ? pick_epi<5, MODE_MFMA>(epi, a, stream) : pick_epi<4, MODE_MFMA>(epi, a, stream);
+}
+
+}  // namespace w4

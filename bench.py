@@ -78,6 +78,9 @@ def main() -> int:
     ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of rotated weight copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--route", type=int, default=-1, help="force one route (bench of a schedule)")
+    ap.add_argument("--probe", choices=["copy", "read"], default=None,
+                    help="run only the plain copy/read kernel of libw4probe.so (counter reference)")
+    ap.add_argument("--probe-mb", type=float, default=256.0)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -88,6 +91,9 @@ def main() -> int:
     import torch
     import w4_groupwise_gemm_amd as w4
     from synth import make_workload
+
+    if args.probe:
+        return run_probe(args)
 
     cfg_name, widths, opname = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -239,6 +245,42 @@ def main() -> int:
     }
     print(json.dumps(line))
     return 0 if parity_ok else 1
+
+
+def run_probe(args) -> int:
+    """Plain copy (or read) kernel over a buffer of known size: the reference for scaling the
+    FETCH_SIZE / WRITE_SIZE counters, and the achievable HBM read rate."""
+    import ctypes
+    import torch
+    P = ctypes.CDLL(os.path.join(ROOT, "w4_groupwise_gemm_amd", "libw4probe.so"))
+    P.w4probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    P.w4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    nbytes = int(args.probe_mb * 1e6) // 4096 * 4096
+    dev = torch.device("cuda:0")
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes if args.probe == "copy" else 16, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    times = []
+    for i in range(args.warmup + args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if args.probe == "copy":
+            rc = P.w4probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, 2048, sh)
+        else:
+            rc = P.w4probe_read(src.data_ptr(), nbytes, dst.data_ptr(), 2048, sh)
+        e1.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed: {rc}")
+        if i >= args.warmup:
+            times.append((e0, e1))
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in times]) * 1e3)
+    moved = nbytes * (2 if args.probe == "copy" else 1)
+    print(json.dumps({"probe": args.probe, "bytes_read": nbytes,
+                      "bytes_written": nbytes if args.probe == "copy" else 0,
+                      "us_median": us, "GBs": moved / us / 1e3}))
+    return 0
 
 
 def cpu_baseline(wl, widths, op, bits, lo, hi, sc, ze, wstream_alg, prefill, rows, K):

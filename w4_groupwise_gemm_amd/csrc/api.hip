@@ -108,7 +108,6 @@ int pick_route(int op, int bits, int T, int N, int K) {
   (void)bits;
   (void)N;
   (void)K;
-  if (T <= 2) return R_GEMV;
   if (T <= 16) return R_N16;
   if (T <= 32) return R_N32;
   if (T <= 64) return R_N64;

@@ -11,10 +11,15 @@ reads the next of C >= 1 GiB / W-stream device copies of the packed weights (the
 of the ninfer-3080 performance notes, "Route boundaries are measured here").  Activations stay
 resident, as when produced by the previous op.
 
-value = effective weight-stream GB/s over the timed steps (packed codes + fp16 scales + fp16
-zeros per launch, times launches, divided by the timed wall time).  Per-launch kernel durations
-come from HIP events recorded on the launch stream around every launch in the timed region;
-the dominant launch's algorithmic bytes over its mean duration gives roofline.achieved.
+Every call of the library is capturable (no allocation, no host synchronisation), so the
+launches are replayed from HIP graphs, the way a decode loop replays one graph per verify
+width; Python launch overhead never sits between two kernels.  The timed region is one replay
+of a graph holding exactly `--steps` steps, bracketed by synchronize; value = effective
+weight-stream GB/s over it (packed codes + fp16 scales + fp16 zeros per launch, times
+launches, divided by the timed wall time).  The per-launch duration of each width comes from
+HIP events on the launch stream around replays of a graph of back-to-back launches of that
+width (one per cold copy); the dominant width's algorithmic bytes over that duration gives
+roofline.achieved.
 
 cpu_baseline times the fp64 oracle on the host cores over repeats of the same step (about
 10-30 s); it is a reference point, not a target.
@@ -72,8 +77,8 @@ def traffic_from_profiles(workload: str, T: int):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of rotated weight copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -165,44 +170,55 @@ def main() -> int:
     parity_ok = all(p["ok"] for p in parity.values())
     print(f"[bench] parity {parity}", file=sys.stderr, flush=True)
 
+    # ---- timing through HIP graphs: every call is capturable (no allocation, no host sync),
+    # so the launches are replayed from graphs and the GPU never waits on Python.
+    def capture(seq):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for T, c in seq:
+                call(T, pws[c])
+        return g
+
     stream = torch.cuda.current_stream()
-    ci = 0
-    for _ in range(args.warmup):
-        for T in widths:
-            call(T, pws[ci % copies])
-            ci += 1
+    g_warm = capture([(T, s % copies) for s in range(max(1, args.warmup)) for T in widths])
+    g_steps = capture([(T, s % copies) for s in range(args.steps) for T in widths])
+    g_width = {T: capture([(T, c) for c in range(copies)]) for T in widths}
+    g_warm.replay()
+    for g in g_width.values():
+        g.replay()
     torch.cuda.synchronize()
 
-    n_launch = args.steps * len(widths)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_launch)]
+    # the timed region: exactly `steps` steps, one graph replay, bracketed by synchronize
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    li = 0
-    for _ in range(args.steps):
-        for T in widths:
-            ev[li][0].record(stream)
-            call(T, pws[ci % copies])
-            ev[li][1].record(stream)
-            ci += 1
-            li += 1
+    g_steps.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # per-launch duration of each width: HIP events around replays of `copies` back-to-back
+    # launches of that width (one per cold copy), on the launch stream
+    reps = 5
     per_T = {}
-    for i, T in enumerate(widths):
-        d = np.array([ev[s * len(widths) + i][0].elapsed_time(ev[s * len(widths) + i][1])
-                      for s in range(args.steps)]) * 1e3  # us
+    for T in widths:
+        samples = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g_width[T].replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            samples.append(e0.elapsed_time(e1) * 1e3 / copies)  # us per launch
+        d = np.array(samples)
         alg_bytes = wstream_alg + T * K * 2 + T * N * 2 * (2 if op == w4.OP_ADD else 1)
         flops = 2.0 * T * rows * K
         rid = args.route if args.route >= 0 else w4.route_for(op, bits, T, N, K)
-        boot = np.median(rng.choice(d, size=(1000, d.size)), axis=1)
         per_T[str(T)] = {
-            "route": w4.route_name(rid), "us_mean": float(d.mean()), "us_median": float(np.median(d)),
-            "us_ci95": [float(np.percentile(boot, 2.5)), float(np.percentile(boot, 97.5))],
+            "route": w4.route_name(rid), "us_mean": float(d.mean()), "us_min": float(d.min()),
+            "us_max": float(d.max()), "launches_timed": reps * copies,
             "weight_GBs": wstream_alg / (d.mean() * 1e3), "alg_GBs": alg_bytes / (d.mean() * 1e3),
             "TFLOPs": flops / (d.mean() * 1e6), "alg_bytes": alg_bytes,
         }
+
     dom = max(widths, key=lambda T: per_T[str(T)]["us_mean"])
     pd = per_T[str(dom)]
     prefill = min(widths) >= 1024

@@ -76,6 +76,10 @@ int validate(int op, const void* x, const void* w, const void* s, const void* z,
     const uintptr_t b = reinterpret_cast<uintptr_t>(p);
     return Range{b, b + n};
   };
+  // 32-bit buffer offsets: every tensor must stay below 2 GiB
+  const size_t kLimit = (size_t)1 << 31;
+  if ((size_t)T * K * 2 >= kLimit || (size_t)T * N * 2 >= kLimit || wbytes >= kLimit)
+    return W4_ERR_UNSUPPORTED;
   const Range ro = rng(out, (size_t)T * N * 2);
   if (overlap(ro, rng(x, (size_t)T * K * 2)) || overlap(ro, rng(w, wbytes)) ||
       overlap(ro, rng(s, szbytes)) || overlap(ro, rng(z, szbytes)))

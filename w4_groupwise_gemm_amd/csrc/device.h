@@ -13,6 +13,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -85,6 +86,13 @@ __device__ __forceinline__ f16x2 splat(uint32_t pair) {
 // l%16, k slots 8*(l/16)..+7; the lane then holds D rows 4*(l/16)+i, column l%16, i = 0..3.
 __device__ __forceinline__ f32x4 mfma16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// 32x32x16 fp16 matrix-core step, fp32 accumulate.  A lane l supplies A row l%32 and B column
+// l%32, k slots 8*(l/32)..+7; the lane then holds D rows 8*(v/4) + 4*(l/32) + v%4 in register
+// v (v = 0..15), column l%32.
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }

@@ -2,26 +2,32 @@
 //
 // Prior art: the prefill schedules of the ninfer-3080 performance notes ("The token tile, and
 // why it was hiding": a token tile of BN columns re-streams the whole weight matrix T/BN times,
-// so the tile must be wide; a grid swizzle for cache reuse bought nothing there because the
-// passes themselves had to go; "What is still missing": the mainloop -- double buffering and a
+// so the tile must be wide; "What is still missing": the mainloop -- double buffering and a
 // conflict-free shared layout).
 //
 // gfx950 design.
-//  * Workgroup = 4 waves in a 2 x 2 arrangement; a wave owns RTW 16-row tiles x NTW 16-token
-//    tiles (80 x 128 for 5120-row projections), so every dequantised weight fragment feeds NTW
-//    matrix-core steps and the dequantisation (13-19 vector ops per packed word) stays below
-//    the matrix-core time of the same block.
-//  * Weights never touch LDS: the packed layout is the A-operand order, each lane loads its
-//    codes with one 16-byte load per 16-row tile and k-block and dequantises in registers.
+//  * The matrix-core step is v_mfma_f32_32x32x16_f16 (on this chip it sustains about twice the
+//    rate of the 16x16x32 form).  Its A operand is a 32-row "pair" of two 16-row packed tiles:
+//    a lane of the instruction takes row l%32 and k half l/32, and that is exactly what one
+//    16-byte load per lane from the packed layout delivers when the 16-lane groups of the two
+//    tiles are picked in the order (tile a, tile b, tile a, tile b): no repacking and no lane
+//    shuffles.  The four dwords of that load are four 16-k steps.  Weights never touch LDS;
+//    they are dequantised in registers, 13 (4-bit) or 19 (5-bit) vector ops per dword.
+//  * Workgroup = 4 waves.  Wave w owns pair w for every token tile of the workgroup, so each
+//    dequantised fragment feeds NTT matrix-core steps.  5120-row projections use 160-row
+//    workgroups (32 of them tile N exactly); the fifth pair is split between the four waves by
+//    k step (each wave does two of its eight steps per block for all token tiles), and the
+//    four partial sums are added in a fixed order through LDS at the end, so no wave
+//    dequantises more than a quarter of it and results stay bitwise reproducible.
 //  * The activation tile X[BN tokens][128 columns] of each k-block is loaded straight into LDS
-//    with global_load_lds_dwordx4 (no register staging), double buffered, one barrier per
-//    k-block.  16-byte chunks are stored XOR-swizzled by token row (chunk c of row r sits at
-//    c ^ (r & 15)), so the 16 lanes of a read phase hit 16 distinct bank groups.
+//    with buffer_load ... lds (no register staging), double buffered, one barrier per k-block.
+//    16-byte chunks are stored XOR-swizzled by token row (chunk c of row r sits at c ^ (r & 15)),
+//    so the 16 lanes of a read phase hit 16 distinct bank groups.
 //  * Tiles are ordered so that the workgroups running at the same time on one XCD (round-robin
 //    dispatch) cover all row blocks of the same token block: that activation tile is fetched
 //    into the XCD's L2 once and shared, instead of being re-read per row block.
-//  * Integer zero-points (checked exactly and wave-uniformly per block) take a 13-op (4-bit) /
-//    19-op (5-bit) dequantisation; fractional ones the general form.
+//  * Integer zero-points (checked exactly, once per workgroup) take the short dequantisation;
+//    fractional ones the general form.
 #include "device.h"
 #include "kernels.h"
 
@@ -54,13 +60,14 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c
   return r;
 }
 
+// Biased fp16 pairs 1024 + q (slots 0,1 / 4,5) and 1024 + 16 q (slots 2,3 / 6,7) of dword J.
 template <int BITS, int J>
 __device__ __forceinline__ void wbiased(uint32_t w, uint32_t hiw, uint32_t magic, uint32_t u[4]) {
   const uint32_t w8 = w >> 8;
-  u[0] = (w & 0x000F000Fu) | magic;
-  u[1] = (w & 0x00F000F0u) | magic;
-  u[2] = (w8 & 0x000F000Fu) | magic;
-  u[3] = (w8 & 0x00F000F0u) | magic;
+  u[0] = and_or(w, 0x000F000Fu, magic);
+  u[1] = and_or(w, 0x00F000F0u, magic);
+  u[2] = and_or(w8, 0x000F000Fu, magic);
+  u[3] = and_or(w8, 0x00F000F0u, magic);
   if constexpr (BITS == 5) {
     constexpr int t = (J == 0 ? 0 : J == 1 ? 2 : J == 2 ? 8 : 10);
     uint32_t x1, x2;
@@ -78,27 +85,25 @@ __device__ __forceinline__ void wbiased(uint32_t w, uint32_t hiw, uint32_t magic
   }
 }
 
+// fp16 weights (q - z) * s of packed dword J (8 k slots of one row).  FAST: z is an integer,
+// so 1024 + z and 64 + z are exact and one packed add (or fma) removes bias and zero-point.
 template <int BITS, int J, bool FAST>
-__device__ __forceinline__ f16x8 wfrag(uint32_t w, uint32_t hiw, uint32_t magic, f16x2 z2, f16x2 b0,
-                                       f16x2 b1, f16x2 s2) {
+__device__ __forceinline__ f16x8 wfrag(uint32_t w, uint32_t hiw, uint32_t magic, uint32_t zp,
+                                       uint32_t sp) {
   uint32_t u[4];
   wbiased<BITS, J>(w, hiw, magic, u);
+  const f16x2 z2 = splat<(J >> 1)>(zp), s2 = splat<(J >> 1)>(sp);
   const f16x2 c16th = {(f16)0.0625f, (f16)0.0625f};
+  const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f}, c64 = {(f16)64.0f, (f16)64.0f};
   if constexpr (FAST) {
+    const f16x2 b0 = -(z2 + c1024), b1 = -(z2 + c64);
     return cat8((as_h2(u[0]) + b0) * s2, (as_h2(u[1]) * c16th + b1) * s2, (as_h2(u[2]) + b0) * s2,
                 (as_h2(u[3]) * c16th + b1) * s2);
   } else {
-    const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f}, c64 = {(f16)64.0f, (f16)64.0f};
     return cat8(((as_h2(u[0]) - c1024) - z2) * s2, ((as_h2(u[1]) * c16th - c64) - z2) * s2,
                 ((as_h2(u[2]) - c1024) - z2) * s2, ((as_h2(u[3]) * c16th - c64) - z2) * s2);
   }
 }
-
-template <int BITS, int RTW>
-struct Codes {
-  u32x4 cw[RTW];
-  uint32_t hw[RTW], sp[RTW], zp[RTW];
-};
 
 // Buffer resource over `bytes` bytes at `base` (gfx9 raw buffer, 32-bit offsets; reads past
 // the end return zero instead of faulting).
@@ -110,20 +115,78 @@ struct Rsrcs {
   __amdgpu_buffer_rsrc_t x, w, s, z;
 };
 
-template <int BITS, int RTW>
-__device__ __forceinline__ void load_codes(Codes<BITS, RTW>& c, const Rsrcs& R, const KArgs& a,
-                                           int tile_base, int ntiles, int kb, int lane) {
-  constexpr int BLK = block_bytes(BITS);
+// A-operand words of one 32-row pair and one k-block, for this lane.  Set S (0 / 1) is the
+// 16-byte load of k-steps (j, S), j = 0..3; the lane's row is pair row lane % 32, its k half
+// h = lane / 32.  In packed terms: 16-lane group (lane / 16) reads tile a, b, a, b of the pair,
+// and the source lane inside that tile is lane % 16 + 16 (S + 2 h), whose k slots are
+// 64 (j / 2) + 16 (S + 2 h) + 8 (j % 2) + e.
+template <int BITS>
+struct PairCodes {
+  u32x4 cw[2];
+  uint32_t hw[2];   // high-bit planes (5-bit only)
+  uint32_t sp, zp;  // this lane's row: fp16 scale / zero-point pairs (groups 0, 1 of the block)
+};
+
+// The share of the fifth pair that one wave computes: its two dwords (k-steps) of one set.
+template <int BITS>
+struct ShareCodes {
+  u32x2 cw;
+  uint32_t hw;
+  uint32_t sp, zp;
+};
+
+// Lane-constant parts of the code addresses.
+struct LaneMap {
+  int slot16[2];  // byte offset of the lane's 16-byte code slot in a block, sets 0 and 1
+  int th;         // tile of the pair (0 / 1) this lane reads
+  int row4;       // 4 * (row within the tile): scale / zero-point slot
+};
+
+__device__ __forceinline__ LaneMap lane_map(int lane) {
+  LaneMap m;
+  m.th = (lane >> 4) & 1;
+  m.row4 = (lane & 15) * 4;
 #pragma unroll
-  for (int rt = 0; rt < RTW; ++rt) {
-    const int tile = min(tile_base + rt, ntiles - 1);
-    const int bi = tile * a.KB + kb;
-    c.cw[rt] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.w, lane * 16, bi * BLK, 0));
-    if constexpr (BITS == 5) c.hw[rt] = __builtin_amdgcn_raw_buffer_load_b32(R.w, 1024 + lane * 4, bi * BLK, 0);
-    else c.hw[rt] = 0;
-    c.sp[rt] = __builtin_amdgcn_raw_buffer_load_b32(R.s, (lane & 15) * 4, bi * 64, 0);
-    c.zp[rt] = __builtin_amdgcn_raw_buffer_load_b32(R.z, (lane & 15) * 4, bi * 64, 0);
+  for (int s = 0; s < 2; ++s) m.slot16[s] = ((lane & 15) + 16 * (s + 2 * (lane >> 5))) * 16;
+  return m;
+}
+
+// Every offset below is lane-dependent, so it goes in the lane operand; the tile index is
+// clamped to the last tile (an odd tile count leaves the second tile of the last pair empty:
+// its rows are computed from the clamped tile and never stored).
+template <int BITS>
+__device__ __forceinline__ void load_pair(PairCodes<BITS>& c, const Rsrcs& R, const KArgs& a,
+                                          const LaneMap& m, int pair, int ntiles, int kb) {
+  constexpr int BLK = block_bytes(BITS);
+  const int tile = min(2 * pair + m.th, ntiles - 1);
+  const int bi = tile * a.KB + kb;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    c.cw[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.w, bi * BLK + m.slot16[s], 0, 0));
+    if constexpr (BITS == 5)
+      c.hw[s] = __builtin_amdgcn_raw_buffer_load_b32(R.w, bi * BLK + 1024 + m.slot16[s] / 4, 0, 0);
+    else
+      c.hw[s] = 0;
   }
+  c.sp = __builtin_amdgcn_raw_buffer_load_b32(R.s, bi * 64 + m.row4, 0, 0);
+  c.zp = __builtin_amdgcn_raw_buffer_load_b32(R.z, bi * 64 + m.row4, 0, 0);
+}
+
+// Wave W's share of pair `pair`: set S = W / 2, dwords j = 2 (W % 2) and 2 (W % 2) + 1.
+template <int BITS, int W>
+__device__ __forceinline__ void load_share(ShareCodes<BITS>& c, const Rsrcs& R, const KArgs& a,
+                                           const LaneMap& m, int pair, int ntiles, int kb) {
+  constexpr int BLK = block_bytes(BITS);
+  const int tile = min(2 * pair + m.th, ntiles - 1);
+  const int bi = tile * a.KB + kb;
+  const int slot = m.slot16[W >> 1];
+  c.cw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(R.w, bi * BLK + slot + 8 * (W & 1), 0, 0));
+  if constexpr (BITS == 5)
+    c.hw = __builtin_amdgcn_raw_buffer_load_b32(R.w, bi * BLK + 1024 + slot / 4, 0, 0);
+  else
+    c.hw = 0;
+  c.sp = __builtin_amdgcn_raw_buffer_load_b32(R.s, bi * 64 + m.row4, 0, 0);
+  c.zp = __builtin_amdgcn_raw_buffer_load_b32(R.z, bi * 64 + m.row4, 0, 0);
 }
 
 // Direct-to-LDS load of the activation tile of k-block kb: BN token rows x 16 chunks of 16 B.
@@ -135,7 +198,7 @@ __device__ __forceinline__ void load_codes(Codes<BITS, RTW>& c, const Rsrcs& R, 
 // past the end of the buffer resource and read as zero.  Columns beyond K inside the buffer
 // (half-empty last block) read the next row; those k slots are skipped by the math.
 template <int BN>
-__device__ __forceinline__ void load_x_lds(const Rsrcs& R, const KArgs& a, _Float16* xs,
+__device__ __forceinline__ void load_x_lds(const Rsrcs& R, const KArgs& a, char* xs,
                                            const int (&voff)[4], int tok0, int kb, int wave) {
   constexpr int PER_WAVE = BN / 16;  // instructions per wave
 #pragma unroll
@@ -143,89 +206,181 @@ __device__ __forceinline__ void load_x_lds(const Rsrcs& R, const KArgs& a, _Floa
     const int r0 = (wave * PER_WAVE + i) * 4;
     const int rowoff = ((tok0 + r0) * a.K + kb * 128) * 2;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        R.x, (__attribute__((address_space(3))) void*)(xs + r0 * 128), 16,
+        R.x, (__attribute__((address_space(3))) void*)(xs + r0 * 256), 16,
         voff[(r0 & 15) >> 2] + rowoff, 0, 0, 0);
   }
 }
 
-template <int BITS, int RTW, int NTW, int J, bool FAST>
-__device__ __forceinline__ void wide_j(const Codes<BITS, RTW>& c, const _Float16* xs, int tokw,
-                                       int lane, uint32_t magic, const f16x2* nb0, const f16x2* nb1,
-                                       f32x4 (&acc)[RTW][NTW]) {
-  const int r = lane & 15, g = lane >> 4;
-  constexpr int cj = 8 * (J >> 1) + (J & 1);
-  f16x8 b[NTW];
+// k-steps of a block, in group order: index i = 2 J + S is the 16-k step (J, S); steps 0..3
+// cover group 0 of the block and steps 4..7 group 1, which a half-empty last block
+// (K % 128 == 64) does not have.  Wave W's share of the fifth pair is the set S = W / 2 of
+// dwords J = 2 (W % 2) and 2 (W % 2) + 1.
+template <int NP, int W, int I>
+constexpr bool share_step() {
+  return NP == 5 && (I & 1) == (W >> 1) && ((I >> 1) >> 1) == (W & 1);
+}
+
+// B lane l of step (J, S): token row 32 tt + l%32, k = 64 (J/2) + 16 (S + 2 h) + 8 (J%2) + e,
+// i.e. LDS chunk c = 8 (J/2) + (J%2) + 2 S + 4 h stored at c ^ (row & 15).  With
+// bsw = row * 256 + 16 ((4 h) ^ (row & 15)) and the constant part of c disjoint from 4 h in
+// bits, the slot is bsw ^ 16 C.
+template <int NTT, int I>
+__device__ __forceinline__ void load_b(const char* xs, int bsw, f16x8 (&B)[NTT]) {
+  constexpr int J = I >> 1, S = I & 1;
+  constexpr int C = 8 * (J >> 1) + (J & 1) + 2 * S;
+  const char* xb = xs + (bsw ^ (16 * C));
 #pragma unroll
-  for (int tt = 0; tt < NTW; ++tt) {
-    const int row = tokw + tt * 16 + r;
-    b[tt] = *reinterpret_cast<const f16x8*>(xs + row * 128 + (((cj + 2 * g) ^ r) * 8));
+  for (int tt = 0; tt < NTT; ++tt) B[tt] = *reinterpret_cast<const f16x8*>(xb + tt * 32 * 256);
+}
+
+// A fragments of step I: the wave's own pair and, on its share steps, the fifth pair.
+template <int BITS, int NP, int W, int I, bool FAST>
+__device__ __forceinline__ void deq_a(const PairCodes<BITS>& cur, const ShareCodes<BITS>& sh,
+                                      uint32_t magic, f16x8& A, f16x8& A4) {
+  constexpr int J = I >> 1, S = I & 1;
+  A = wfrag<BITS, J, FAST>(cur.cw[S][J], cur.hw[S], magic, cur.zp, cur.sp);
+  if constexpr (share_step<NP, W, I>())
+    A4 = wfrag<BITS, J, FAST>(sh.cw[J & 1], sh.hw, magic, sh.zp, sh.sp);
+}
+
+// Step I of the software pipeline: the matrix-core steps of step I run while the B fragments of
+// step I + 1 are read and its A fragments dequantised.  The schedule interleaves one
+// matrix-core step with a few vector ops and one LDS read, so that with one wave per SIMD the
+// vector work issues in the shadow of the matrix cores.
+template <int BITS, int NP, int NTT, int W, int I, bool FAST>
+__device__ __forceinline__ void wide_step(const PairCodes<BITS>& cur, const ShareCodes<BITS>& sh,
+                                          const char* xs, int bsw, uint32_t magic,
+                                          const f16x8& Acur, f16x8& Anxt, f16x8& A4,
+                                          const f16x8 (&Bcur)[NTT], f16x8 (&Bnxt)[NTT],
+                                          f32x16 (&acc)[NTT], f32x16 (&accs)[NTT]) {
+  constexpr bool SH = share_step<NP, W, I>();
+  const f16x8 A4cur = A4;
+  if constexpr (I + 1 < 8) {
+    load_b<NTT, I + 1>(xs, bsw, Bnxt);
+    deq_a<BITS, NP, W, I + 1, FAST>(cur, sh, magic, Anxt, A4);
   }
 #pragma unroll
-  for (int rt = 0; rt < RTW; ++rt) {
-    const f16x8 A = wfrag<BITS, J, FAST>(c.cw[rt][J], c.hw[rt], magic, splat<(J >> 1)>(c.zp[rt]),
-                                         splat<(J >> 1)>(__builtin_bit_cast(uint32_t, nb0[rt])),
-                                         splat<(J >> 1)>(__builtin_bit_cast(uint32_t, nb1[rt])),
-                                         splat<(J >> 1)>(c.sp[rt]));
+  for (int tt = 0; tt < NTT; ++tt) acc[tt] = mfma32(Acur, Bcur[tt], acc[tt]);
+  if constexpr (SH) {
 #pragma unroll
-    for (int tt = 0; tt < NTW; ++tt) acc[rt][tt] = mfma16(A, b[tt], acc[rt][tt]);
+    for (int tt = 0; tt < NTT; ++tt) accs[tt] = mfma32(A4cur, Bcur[tt], accs[tt]);
   }
-  // keep the scheduler from hoisting the next step's fragments over these matrix-core steps
-  // (that would hold four steps of B fragments live and spill)
+  constexpr int M = NTT * (SH ? 2 : 1);
+  constexpr int V = (I + 1 < 8) ? (BITS == 5 ? 20 : 14) * (share_step<NP, W, I + 1>() ? 2 : 1) : 0;
+  constexpr int VPER = (V + M - 1) / M;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix-core step
+    if (i < NTT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // vector ops
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int BITS, int RTW, int NTW, bool FAST>
-__device__ __forceinline__ void wide_block(const Codes<BITS, RTW>& c, const _Float16* xs, int tokw,
-                                           int lane, uint32_t magic, bool half_block,
-                                           f32x4 (&acc)[RTW][NTW]) {
-  f16x2 nb0[RTW], nb1[RTW];
-  const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f}, c64 = {(f16)64.0f, (f16)64.0f};
-#pragma unroll
-  for (int rt = 0; rt < RTW; ++rt) {
-    nb0[rt] = -(as_h2(c.zp[rt]) + c1024);
-    nb1[rt] = -(as_h2(c.zp[rt]) + c64);
-  }
-  wide_j<BITS, RTW, NTW, 0, FAST>(c, xs, tokw, lane, magic, nb0, nb1, acc);
-  wide_j<BITS, RTW, NTW, 1, FAST>(c, xs, tokw, lane, magic, nb0, nb1, acc);
-  if (!half_block) {
-    wide_j<BITS, RTW, NTW, 2, FAST>(c, xs, tokw, lane, magic, nb0, nb1, acc);
-    wide_j<BITS, RTW, NTW, 3, FAST>(c, xs, tokw, lane, magic, nb0, nb1, acc);
-  }
-}
-
-template <int BITS, int RTW, int NTW, int BN, bool FAST>
-__device__ __forceinline__ void wide_loop(const Rsrcs& R, const KArgs& a, _Float16* xbase,
-                                          const int (&voff)[4], int tok0, int tile_base, int ntiles,
-                                          int tokw, int wave, int lane, uint32_t magic,
-                                          Codes<BITS, RTW> cur, f32x4 (&acc)[RTW][NTW]) {
-  Codes<BITS, RTW> nxt;
+template <int BITS, int NP, int NTT, int W, bool FAST>
+__device__ __forceinline__ void wide_loop(const Rsrcs& R, const KArgs& a, char* xbase,
+                                          const int (&voff)[4], int bsw, int tok0, int pair,
+                                          int spair, int ntiles, int wave, const LaneMap& m,
+                                          uint32_t magic, PairCodes<BITS> cur,
+                                          f32x16 (&acc)[NTT], f32x16 (&accs)[NTT]) {
+  constexpr int BN = 32 * NTT;
+  PairCodes<BITS> nxt;
+  ShareCodes<BITS> sh{}, shn;
+  if constexpr (NP == 5) load_share<BITS, W>(sh, R, a, m, spair, ntiles, 0);
+  f16x8 A0, A1, A4, B0[NTT], B1[NTT];
   for (int kb = 0; kb < a.KB; ++kb) {
-    // everything this wave issued has landed: its share of X(kb) and the codes of block kb
-    // (both are needed now; waiting for all keeps this independent of the load order) ...
+    // everything this wave issued has landed (its share of X(kb), the codes of block kb) ...
     wait_vmcnt<0>();
     // ... and so has everyone else's; everyone is also done reading the other buffer
     __syncthreads();
     const bool more = kb + 1 < a.KB;
     if (more) {
-      load_x_lds<BN>(R, a, xbase + ((kb + 1) & 1) * (BN * 128), voff, tok0, kb + 1, wave);
-      load_codes(nxt, R, a, tile_base, ntiles, kb + 1, lane);
+      load_x_lds<BN>(R, a, xbase + ((kb + 1) & 1) * (BN * 256), voff, tok0, kb + 1, wave);
+      load_pair(nxt, R, a, m, pair, ntiles, kb + 1);
+      if constexpr (NP == 5) load_share<BITS, W>(shn, R, a, m, spair, ntiles, kb + 1);
     }
-    const _Float16* xs = xbase + (kb & 1) * (BN * 128);
-    wide_block<BITS, RTW, NTW, FAST>(cur, xs, tokw, lane, magic, kb * 128 + 64 >= a.K, acc);
-    if (more) cur = nxt;
+    const char* xs = xbase + (kb & 1) * (BN * 256);
+    load_b<NTT, 0>(xs, bsw, B0);
+    deq_a<BITS, NP, W, 0, FAST>(cur, sh, magic, A0, A4);
+    wide_step<BITS, NP, NTT, W, 0, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B0, B1, acc, accs);
+    wide_step<BITS, NP, NTT, W, 1, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B1, B0, acc, accs);
+    wide_step<BITS, NP, NTT, W, 2, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B0, B1, acc, accs);
+    // (step 3 also prepares step 4; in a half-empty block that reads LDS and codes that exist
+    // but are never used)
+    wide_step<BITS, NP, NTT, W, 3, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B1, B0, acc, accs);
+    if (kb * 128 + 64 < a.K) {
+      wide_step<BITS, NP, NTT, W, 4, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B0, B1, acc, accs);
+      wide_step<BITS, NP, NTT, W, 5, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B1, B0, acc, accs);
+      wide_step<BITS, NP, NTT, W, 6, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B0, B1, acc, accs);
+      wide_step<BITS, NP, NTT, W, 7, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B1, B0, acc, accs);
+    }
+    if (more) {
+      cur = nxt;
+      if constexpr (NP == 5) sh = shn;
+    }
   }
 }
 
-template <int BITS, int RTW, int NTW, int EPI>
-__global__ __launch_bounds__(256, 1) void wide_kernel(KArgs a, int nrb, int ntb) {
-  constexpr int BN = 32 * NTW;    // tokens per workgroup
-  constexpr int TILES = 2 * RTW;  // row tiles per workgroup
+// The wave index selects the share steps at compile time (one copy of the loop per wave for
+// five-pair workgroups, one copy in all for four).
+template <int BITS, int NP, int NTT, bool FAST>
+__device__ __forceinline__ void wide_loop_w(const Rsrcs& R, const KArgs& a, char* xbase,
+                                            const int (&voff)[4], int bsw, int tok0, int pair,
+                                            int spair, int ntiles, int wave, const LaneMap& m,
+                                            uint32_t magic, const PairCodes<BITS>& cur,
+                                            f32x16 (&acc)[NTT], f32x16 (&accs)[NTT]) {
+#define W4_WIDE_LOOP(W)                                                                         \
+  wide_loop<BITS, NP, NTT, W, FAST>(R, a, xbase, voff, bsw, tok0, pair, spair, ntiles, wave, m, \
+                                    magic, cur, acc, accs)
+  if constexpr (NP == 5) {
+    switch (wave) {
+      case 0: W4_WIDE_LOOP(0); break;
+      case 1: W4_WIDE_LOOP(1); break;
+      case 2: W4_WIDE_LOOP(2); break;
+      default: W4_WIDE_LOOP(3); break;
+    }
+  } else {
+    W4_WIDE_LOOP(0);
+  }
+#undef W4_WIDE_LOOP
+}
+
+// Epilogue of one 32 x 32 accumulator: pair `pair`, tokens tok .. tok + 31.  Lane l holds token
+// tok + l%32 and, in registers 4q .. 4q+3, pair rows 8q + 4 (l/32) + 0..3 (4 consecutive output
+// columns).  SwiGLU pairs are (gate tile, up tile): gate row r sits in register v and the up
+// row of the same output column r in register v + 8 of the same lane.
+template <int EPI>
+__device__ __forceinline__ void store_pair(const KArgs& a, const f32x16& v, int pair, int tok,
+                                           int ntiles, int lane) {
+  const int t = tok + (lane & 31);
+  if (t >= a.T || 2 * pair >= ntiles) return;
+  const int h = lane >> 5;
+  const size_t rowoff = (size_t)t * a.ldo;
+  if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      store_quad<EPI>(a.out, a.res, rowoff + 16 * pair + 8 * q + 4 * h,
+                      f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]},
+                      f32x4{v[8 + 4 * q], v[9 + 4 * q], v[10 + 4 * q], v[11 + 4 * q]});
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (q >= 2 && 2 * pair + 1 >= ntiles) break;  // odd tile count: no second tile
+      store_quad<EPI>(a.out, a.res, rowoff + 32 * pair + 8 * q + 4 * h,
+                      f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]}, f32x4{});
+    }
+  }
+}
+
+template <int BITS, int NP, int NTT, int EPI, int OCC>
+__global__ __launch_bounds__(256, OCC) void wide_kernel(KArgs a, int nrb, int ntb) {
+  constexpr int BN = 32 * NTT;   // tokens per workgroup
+  constexpr int TILES = 2 * NP;  // 16-row tiles per workgroup
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  _Float16* const xbase = reinterpret_cast<_Float16*>(smem);  // two buffers of BN x 128 fp16
+  char* const xbase = smem;  // two buffers of BN x 256 bytes
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wr = wave & 1, wt = wave >> 1;
   const int ntiles = a.rows / 16;
 
   // XCD-aware order: XCD x (= blockIdx % 8) takes a contiguous run of tiles, token-block major.
@@ -235,9 +390,9 @@ __global__ __launch_bounds__(256, 1) void wide_kernel(KArgs a, int nrb, int ntb)
   const int t_idx = xcd * q + min(xcd, rem) + l;
   const int rb = t_idx % nrb, tb = t_idx / nrb;
   const int tok0 = tb * BN;
-  const int tile_base = rb * TILES + wr * RTW;
-  const int tokw = wt * NTW * 16;
+  const int pair = rb * NP + wave, spair = rb * NP + 4;
   const uint32_t magic = vgpr_const(0x64006400u);
+  const LaneMap m = lane_map(lane);
 
   Rsrcs R;
   R.x = rsrc(a.x, (uint32_t)((size_t)a.T * a.K * 2));
@@ -246,21 +401,24 @@ __global__ __launch_bounds__(256, 1) void wide_kernel(KArgs a, int nrb, int ntb)
   R.z = rsrc(a.zr, (uint32_t)((size_t)ntiles * a.KB * 64));
   int voff[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int rl = lane >> 4;                          // row within the instruction
-    const int chunk = (lane & 15) ^ (4 * m + rl);      // source chunk stored at this lane's slot
-    voff[m] = (rl * a.K + chunk * 8) * 2;
+  for (int i = 0; i < 4; ++i) {
+    const int rl = lane >> 4;                      // row within the instruction
+    const int chunk = (lane & 15) ^ (4 * i + rl);  // source chunk stored at this lane's slot
+    voff[i] = (rl * a.K + chunk * 8) * 2;
+  }
+  const int brow = lane & 31;
+  const int bsw = brow * 256 + 16 * ((4 * (lane >> 5)) ^ (brow & 15));
+
+  f32x16 acc[NTT], accs[NTT];
+#pragma unroll
+  for (int tt = 0; tt < NTT; ++tt) {
+    acc[tt] = f32x16{};
+    accs[tt] = f32x16{};
   }
 
-  f32x4 acc[RTW][NTW];
-#pragma unroll
-  for (int rt = 0; rt < RTW; ++rt)
-#pragma unroll
-    for (int tt = 0; tt < NTW; ++tt) acc[rt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   load_x_lds<BN>(R, a, xbase, voff, tok0, 0, wave);
-  Codes<BITS, RTW> cur;
-  load_codes(cur, R, a, tile_base, ntiles, 0, lane);
+  PairCodes<BITS> cur;
+  load_pair(cur, R, a, m, pair, ntiles, 0);
 
   // Are all zero-points of this workgroup's rows integers (1024 + z exact in fp16)?  One vote
   // for the whole kernel run of this workgroup, so the two main loops below are separate code
@@ -279,69 +437,69 @@ __global__ __launch_bounds__(256, 1) void wide_kernel(KArgs a, int nrb, int ntb)
     }
   }
   if (__syncthreads_and(exact))
-    wide_loop<BITS, RTW, NTW, BN, true>(R, a, xbase, voff, tok0, tile_base, ntiles, tokw, wave,
-                                        lane, magic, cur, acc);
+    wide_loop_w<BITS, NP, NTT, true>(R, a, xbase, voff, bsw, tok0, pair, spair, ntiles, wave, m,
+                                     magic, cur, acc, accs);
   else
-    wide_loop<BITS, RTW, NTW, BN, false>(R, a, xbase, voff, tok0, tile_base, ntiles, tokw, wave,
-                                         lane, magic, cur, acc);
+    wide_loop_w<BITS, NP, NTT, false>(R, a, xbase, voff, bsw, tok0, pair, spair, ntiles, wave,
+                                      m, magic, cur, acc, accs);
 
-  const int r = lane & 15, quad = 4 * (lane >> 4);
-  if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-    for (int p = 0; p < RTW / 2; ++p) {
-      const int gtile = tile_base + 2 * p;
-      if (gtile >= ntiles) continue;
+  for (int tt = 0; tt < NTT; ++tt) store_pair<EPI>(a, acc[tt], pair, tok0 + 32 * tt, ntiles, lane);
+
+  if constexpr (NP == 5) {
+    // Fifth pair: wave w holds the partial sums of k-steps (j, w/2), j in {2 (w%2), 2 (w%2)+1}
+    // of every block.  The four are added in wave order through LDS (the activation buffers
+    // are free once every wave has left the loop); wave w finishes token tiles w*NTT/4 ...
+    static_assert(4 * NTT * 16 * 64 * 4 <= 2 * BN * 256, "reduction fits the activation buffers");
+    float* red = reinterpret_cast<float*>(smem);
+    __syncthreads();
 #pragma unroll
-      for (int tt = 0; tt < NTW; ++tt) {
-        const int t = tok0 + tokw + tt * 16 + r;
-        if (t < a.T)
-          store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + (gtile >> 1) * 16 + quad,
-                          acc[2 * p][tt], acc[2 * p + 1][tt]);
+    for (int tt = 0; tt < NTT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[((wave * NTT + tt) * 16 + v) * 64 + lane] = accs[tt][v];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NTT / 4; ++i) {
+      const int tt = wave * (NTT / 4) + i;
+      f32x16 sum;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float s = red[((0 * NTT + tt) * 16 + v) * 64 + lane];
+        s += red[((1 * NTT + tt) * 16 + v) * 64 + lane];
+        s += red[((2 * NTT + tt) * 16 + v) * 64 + lane];
+        s += red[((3 * NTT + tt) * 16 + v) * 64 + lane];
+        sum[v] = s;
       }
-    }
-  } else {
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-      const int tile = tile_base + rt;
-      if (tile >= ntiles) continue;
-#pragma unroll
-      for (int tt = 0; tt < NTW; ++tt) {
-        const int t = tok0 + tokw + tt * 16 + r;
-        if (t < a.T)
-          store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + tile * 16 + quad, acc[rt][tt],
-                          f32x4{});
-      }
+      store_pair<EPI>(a, sum, spair, tok0 + 32 * tt, ntiles, lane);
     }
   }
 }
 
-template <int BITS, int RTW, int NTW, int EPI>
+template <int BITS, int NP, int NTT, int EPI>
 hipError_t run(const KArgs& a, hipStream_t stream) {
-  constexpr int BN = 32 * NTW, TILES = 2 * RTW;
+  constexpr int BN = 32 * NTT, TILES = 2 * NP;
+  // two waves per SIMD (two workgroups per compute unit) when the tile's registers allow it
+  constexpr int OCC = (NTT <= 4) ? 2 : 1;
   const int ntiles = a.rows / 16;
   const int nrb = (ntiles + TILES - 1) / TILES;
   const int ntb = (a.T + BN - 1) / BN;
-  const size_t lds = (size_t)2 * BN * 128 * sizeof(_Float16);
-  hipLaunchKernelGGL((wide_kernel<BITS, RTW, NTW, EPI>), dim3(nrb * ntb), dim3(256), lds, stream,
-                     a, nrb, ntb);
+  const size_t lds = (size_t)2 * BN * 256;
+  hipLaunchKernelGGL((wide_kernel<BITS, NP, NTT, EPI, OCC>), dim3(nrb * ntb), dim3(256), lds,
+                     stream, a, nrb, ntb);
   return hipGetLastError();
 }
 
 template <int BITS, int EPI>
 hipError_t pick(const KArgs& a, hipStream_t stream) {
-  if constexpr (EPI == EPI_SWIGLU) {
-    return run<BITS, 4, 8, EPI>(a, stream);
-  } else {
-    const int ntiles = a.rows / 16;
-    // 160-row tiles divide the 5120-row projections into 32 row blocks.
-    if (ntiles % 10 == 0) {
-      // keep at least one workgroup per compute unit: narrower token tile for short prefill
-      const long wg_wide = (long)(ntiles / 10) * ((a.T + 255) / 256);
-      if (wg_wide >= 256) return run<BITS, 5, 8, EPI>(a, stream);
-      return run<BITS, 5, 4, EPI>(a, stream);
-    }
-    return run<BITS, 4, 8, EPI>(a, stream);
-  }
+  const int ntiles = a.rows / 16;
+  // 160-row workgroups (5 pairs) divide the 5120-row projections into 32 row blocks; the
+  // SwiGLU pair layout (gate, up) keeps every 32-row pair inside one output tile either way.
+  const bool five = (ntiles % 10 == 0);
+  const int nrb = five ? ntiles / 10 : (ntiles + 7) / 8;
+  // the 256-token tile when it still gives every compute unit two workgroups, else 128
+  const bool wide = (long)nrb * ((a.T + 255) / 256) >= 512;
+  if (five) return wide ? run<BITS, 5, 8, EPI>(a, stream) : run<BITS, 5, 4, EPI>(a, stream);
+  return wide ? run<BITS, 4, 8, EPI>(a, stream) : run<BITS, 4, 4, EPI>(a, stream);
 }
 
 template <int BITS>

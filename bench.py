@@ -18,8 +18,12 @@ of a graph holding exactly `--steps` steps, bracketed by synchronize; value = ef
 weight-stream GB/s over it (packed codes + fp16 scales + fp16 zeros per launch, times
 launches, divided by the timed wall time).  The per-launch duration of each width comes from
 HIP events on the launch stream around replays of a graph of back-to-back launches of that
-width (one per cold copy); the dominant width's algorithmic bytes over that duration gives
-roofline.achieved.
+width (one per cold copy); the widest launch of the step (most work per launch) is the roofline
+kernel: its algorithmic bytes (or flops) over that duration give roofline.achieved, and
+roofline.traffic is its HBM bytes per launch from the committed counter record
+(profiles/traffic_<workload>.json, written by --traffic-summary from rocprofv3 FETCH_SIZE /
+WRITE_SIZE runs scaled by the same counters of a plain copy kernel), or null when the kernel
+sources changed since the counters were taken.
 
 cpu_baseline times the fp64 oracle on the host cores over repeats of the same step (about
 10-30 s); it is a reference point, not a target.
@@ -86,7 +90,21 @@ def main() -> int:
     ap.add_argument("--probe", choices=["copy", "read"], default=None,
                     help="run only the plain copy/read kernel of libw4probe.so (counter reference)")
     ap.add_argument("--probe-mb", type=float, default=256.0)
+    ap.add_argument("--widths", default=None,
+                    help="comma list of T overriding the workload's widths (counter runs)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch eagerly instead of replaying HIP graphs (counter runs)")
+    ap.add_argument("--traffic-summary", default=None, metavar="DIR",
+                    help="no GPU work: turn the FETCH_SIZE / WRITE_SIZE counter runs under DIR "
+                         "(subdirs fetch, write, copy_fetch, copy_write) into the traffic record")
+    ap.add_argument("--kernel-match", default=None,
+                    help="substring of the measured kernel's name (with --traffic-summary)")
+    ap.add_argument("--copy-mb", type=float, default=256.0,
+                    help="--probe-mb of the copy runs (with --traffic-summary)")
     args = ap.parse_args()
+
+    if args.traffic_summary:
+        return traffic_summary(args)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this library has no multi-GPU path (each GPU runs the "
@@ -101,6 +119,8 @@ def main() -> int:
         return run_probe(args)
 
     cfg_name, widths, opname = WORKLOADS[args.workload]
+    if args.widths:
+        widths = tuple(int(v) for v in args.widths.split(","))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {cfg_name}", file=sys.stderr, flush=True)
@@ -172,7 +192,19 @@ def main() -> int:
 
     # ---- timing through HIP graphs: every call is capturable (no allocation, no host sync),
     # so the launches are replayed from graphs and the GPU never waits on Python.
+    class Eager:
+        """Same interface as a captured graph, launching eagerly (counter runs)."""
+
+        def __init__(self, seq):
+            self.seq = list(seq)
+
+        def replay(self):
+            for T, c in self.seq:
+                call(T, pws[c])
+
     def capture(seq):
+        if args.no_graph:
+            return Eager(seq)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for T, c in seq:
@@ -219,7 +251,8 @@ def main() -> int:
             "TFLOPs": flops / (d.mean() * 1e6), "alg_bytes": alg_bytes,
         }
 
-    dom = max(widths, key=lambda T: per_T[str(T)]["us_mean"])
+    # roofline of the widest launch of the step (the most work per launch)
+    dom = max(widths)
     pd = per_T[str(dom)]
     prefill = min(widths) >= 1024
     if prefill:
@@ -296,6 +329,62 @@ def run_probe(args) -> int:
     print(json.dumps({"probe": args.probe, "bytes_read": nbytes,
                       "bytes_written": nbytes if args.probe == "copy" else 0,
                       "us_median": us, "GBs": moved / us / 1e3}))
+    return 0
+
+
+def _counter_per_dispatch(run_dir: str, counter: str, match: str):
+    """Mean over dispatches of `counter` (rows of one dispatch summed) for kernels whose name
+    contains `match`, from rocprofv3 --pmc csv output under run_dir."""
+    import csv
+    import glob
+    per = {}
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {run_dir}")
+    name = None
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter or match not in r["Kernel_Name"]:
+                    continue
+                name = r["Kernel_Name"]
+                key = (f, r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise ValueError(f"no {counter} rows for a kernel matching {match!r} under {run_dir}")
+    return sum(per.values()) / len(per), len(per), name
+
+
+def traffic_summary(args) -> int:
+    """Counter runs -> profiles/traffic_<workload>.json: HBM bytes per launch of the measured
+    kernel, FETCH_SIZE and WRITE_SIZE each scaled by what that counter reads for the plain copy
+    kernel of libw4probe.so over a buffer of known size."""
+    if not args.kernel_match or not args.widths:
+        print("--traffic-summary needs --kernel-match and --widths", file=sys.stderr)
+        return 2
+    d = args.traffic_summary
+    fetch, nf, kname = _counter_per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE", args.kernel_match)
+    write, nw, _ = _counter_per_dispatch(os.path.join(d, "write"), "WRITE_SIZE", args.kernel_match)
+    cf, ncf, _ = _counter_per_dispatch(os.path.join(d, "copy_fetch"), "FETCH_SIZE", "copy_kernel")
+    cw, ncw, _ = _counter_per_dispatch(os.path.join(d, "copy_write"), "WRITE_SIZE", "copy_kernel")
+    copy_bytes = int(args.copy_mb * 1e6) // 4096 * 4096
+    fscale, wscale = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
+    rd, wr = fetch * 1024.0 * fscale, write * 1024.0 * wscale
+    T = args.widths
+    rec = {
+        "workload": args.workload, "T": T, "kernel": kname, "kernel_src_sha": kernel_source_sha(),
+        "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
+        "dispatches": {"fetch": nf, "write": nw, "copy_fetch": ncf, "copy_write": ncw},
+        "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,
+        "fetch_scale": fscale, "write_scale": wscale,
+        "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+        "bytes_per_launch": {str(t): rd + wr for t in T.split(",")},
+    }
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    out = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
     return 0
 
 

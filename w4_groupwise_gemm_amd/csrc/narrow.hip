@@ -38,9 +38,6 @@ using namespace w4dev;
 using namespace t32;
 using w4layout::block_bytes;
 
-constexpr int kConsumers = 4;
-constexpr int kThreads = 64 * (kConsumers + 2);
-
 // Byte layout of one code stage: NP pairs x 2 tiles of 1 KB low-plane codes (64 lanes x 16 B,
 // as in the packed block), then (5-bit) 2 NP x 256 B high planes, then 256 B of scale pairs and
 // 256 B of zero-point pairs (lane 16 i + r of the load = tile i, row r).
@@ -60,7 +57,10 @@ struct CodeStage {
 // explicit instead (producers: vmcnt for their own loads; consumers: lgkmcnt for their LDS
 // reads).  The "memory" clobber keeps the compiler from moving memory operations across it.
 __device__ __forceinline__ void arrive_wait() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // lgkmcnt(0) as a builtin, so that the compiler's own wait insertion knows every earlier LDS
+  // read has completed; the barrier itself as volatile asm with a memory clobber
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // Direct-to-LDS loads: lane L's bytes land at lds + SIZE * L.
@@ -112,91 +112,141 @@ __device__ __forceinline__ void load_x(const Rsrcs& R, const KArgs& a, char* xs,
   }
 }
 
-// Producer loop: stage (kb + L) % (L + 1) is refilled right after the barrier of block kb, which
-// every consumer reaches only after finishing block kb - 1 (the stage's previous contents).
-// OPS loads per block; L - 1 blocks of loads may still be in flight when block kb is needed.
-template <int L, int OPS, typename Issue>
+// Producer loop.  Ring of D stages, block b in stage b % D.  The prologue issued blocks
+// 0 .. D-1.  Barrier B(-1) says block 0 is in LDS; barrier B(kb) says block kb + 1 is in LDS
+// and that every consumer has finished reading block kb (consumers read one block ahead of
+// their math), whose stage is then refilled with block kb + D.  OPS loads per block: D - 2
+// blocks of loads may still be in flight at the wait for block kb + 1.
+template <int D, int OPS, typename Issue>
 __device__ __forceinline__ void produce(int KB, Issue issue) {
-  constexpr int NWAIT = (L - 1) * OPS;
-  static_assert(NWAIT < 64, "vmcnt range");
+  static_assert(D >= 2, "ring too shallow");
+  constexpr int NWAIT = (D - 2) * OPS;
+  static_assert(NWAIT + OPS < 64, "vmcnt range");
+  wait_vmcnt<NWAIT + OPS>();  // block 0
+  arrive_wait();              // B(-1)
   for (int kb = 0; kb < KB; ++kb) {
-    wait_vmcnt<NWAIT>();  // block kb is in LDS
-    arrive_wait();
-    issue((kb + L) % (L + 1), min(kb + L, KB - 1));
+    wait_vmcnt<NWAIT>();  // block kb + 1
+    arrive_wait();        // B(kb)
+    issue(kb % D, min(kb + D, KB - 1));
   }
 }
 
-// One consumer: wave W's two k-steps of every block.
-template <int BITS, int NP, int NTT, int LC, int LX, int W, bool FAST>
+// Steps of consumer C among NC: with 4 consumers, 2 consecutive 16-k steps (dwords J0, J0+1 of
+// set S of every pair's packed block); with 8, one.
+template <int NC, int C>
+struct Steps {
+  static constexpr int kN = 8 / NC;
+  static constexpr int kJ0 = NC == 4 ? 2 * (C & 1) : (C & 3);
+  static constexpr int kS = NC == 4 ? (C >> 1) : (C >> 2);
+};
+
+template <int N>
+struct CodeWords;
+template <>
+struct CodeWords<1> {
+  using T = uint32_t;
+  static __device__ __forceinline__ uint32_t at(T v, int) { return v; }
+};
+template <>
+struct CodeWords<2> {
+  using T = u32x2;
+  static __device__ __forceinline__ uint32_t at(T v, int j) { return v[j]; }
+};
+
+// Operands of one block for one consumer, read from LDS one block ahead of the math.
+template <int BITS, int NP, int NTT, int N>
+struct Frag {
+  typename CodeWords<N>::T cw[NP];
+  uint32_t hw[NP], sp[NP], zp[NP];
+  f16x8 B[N][NTT];
+};
+
+// One consumer (wave C): its steps of every block.  Iteration kb reads block kb + 1 (certified by
+// barrier B(kb)) into registers, then runs the math of block kb from the registers read in the
+// previous iteration, so the LDS latency hides behind a block of matrix-core work.
+template <int BITS, int NP, int NTT, int NC, int DC, int DX, int C, bool FAST>
 __device__ __forceinline__ void consume(const KArgs& a, const char* cring, const char* xring,
                                         f32x16 (&acc)[NP][NTT]) {
   using CS = CodeStage<BITS, NP>;
+  using ST = Steps<NC, C>;
+  using CWd = CodeWords<ST::kN>;
+  using F = Frag<BITS, NP, NTT, ST::kN>;
   constexpr int BN = 32 * NTT, XB = BN * 256;
-  constexpr int J0 = 2 * (W & 1), S = W >> 1;
   const int lane = threadIdx.x & 63;
   const LaneMap m = lane_map(lane);
   const uint32_t magic = vgpr_const(0x64006400u);
   const int brow = lane & 31;
   const int bsw = brow * 256 + 16 * ((4 * (lane >> 5)) ^ (brow & 15));
-  const int slot = m.slot16[S];
+  const int slot = m.slot16[ST::kS];
   // lane-constant byte offsets inside a code stage
-  const int lo_off = CS::kLo + m.th * 1024 + slot + 8 * (W & 1);
+  const int lo_off = CS::kLo + m.th * 1024 + slot + 4 * ST::kJ0;
   const int hi_off = CS::kHi + m.th * 256 + slot / 4;
   const int sz_off = m.th * 64 + m.row4;
   const int KB = a.KB;
   const bool half_last = (KB * 128 != a.K);  // last block holds one group only
-  int cst = 0, xst = 0;                       // stage indices of block kb
-  for (int kb = 0; kb < KB; ++kb) {
-    arrive_wait();  // block kb is in LDS; everyone has finished block kb - 1
-    if ((W & 1) == 0 || !(half_last && kb == KB - 1)) {
-      const char* cs = cring + cst * CS::kBytes;
-      const char* xs = xring + xst * XB;
-      u32x2 cw[NP];
-      uint32_t hw[NP], sp[NP], zp[NP];
+
+  auto read = [&](int b, F& f) {
+    const char* cs = cring + (b % DC) * CS::kBytes;
+    const char* xs = xring + (b % DX) * XB;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      f.cw[p] = *reinterpret_cast<const typename CWd::T*>(cs + lo_off + p * 2048);
+      f.hw[p] = BITS == 5 ? *reinterpret_cast<const uint32_t*>(cs + hi_off + p * 512) : 0u;
+      f.sp[p] = *reinterpret_cast<const uint32_t*>(cs + CS::kS + sz_off + p * 128);
+      f.zp[p] = *reinterpret_cast<const uint32_t*>(cs + CS::kZ + sz_off + p * 128);
+    }
+    load_b<NTT, 2 * ST::kJ0 + ST::kS>(xs, bsw, f.B[0]);
+    if constexpr (ST::kN == 2) load_b<NTT, 2 * (ST::kJ0 + 1) + ST::kS>(xs, bsw, f.B[ST::kN - 1]);
+  };
+  auto math = [&](const F& f) {
+#pragma unroll
+    for (int j = 0; j < ST::kN; ++j) {
 #pragma unroll
       for (int p = 0; p < NP; ++p) {
-        cw[p] = *reinterpret_cast<const u32x2*>(cs + lo_off + p * 2048);
-        hw[p] = BITS == 5 ? *reinterpret_cast<const uint32_t*>(cs + hi_off + p * 512) : 0u;
-        sp[p] = *reinterpret_cast<const uint32_t*>(cs + CS::kS + sz_off + p * 128);
-        zp[p] = *reinterpret_cast<const uint32_t*>(cs + CS::kZ + sz_off + p * 128);
-      }
-      f16x8 B0[NTT], B1[NTT];
-      load_b<NTT, 2 * J0 + S>(xs, bsw, B0);
-      load_b<NTT, 2 * (J0 + 1) + S>(xs, bsw, B1);
+        const f16x8 A = j == 0 ? wfrag<BITS, ST::kJ0, FAST>(CWd::at(f.cw[p], 0), f.hw[p], magic, f.zp[p], f.sp[p])
+                               : wfrag<BITS, (ST::kJ0 + 1) & 3, FAST>(CWd::at(f.cw[p], 1), f.hw[p], magic, f.zp[p], f.sp[p]);
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const f16x8 A0 = wfrag<BITS, J0, FAST>(cw[p][0], hw[p], magic, zp[p], sp[p]);
-        const f16x8 A1 = wfrag<BITS, J0 + 1, FAST>(cw[p][1], hw[p], magic, zp[p], sp[p]);
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) acc[p][tt] = mfma32(A0, B0[tt], acc[p][tt]);
-#pragma unroll
-        for (int tt = 0; tt < NTT; ++tt) acc[p][tt] = mfma32(A1, B1[tt], acc[p][tt]);
+        for (int tt = 0; tt < NTT; ++tt) acc[p][tt] = mfma32(A, f.B[j][tt], acc[p][tt]);
       }
     }
-    cst = cst == LC ? 0 : cst + 1;
-    xst = xst == LX ? 0 : xst + 1;
+  };
+
+  // two register sets used in turn (no copies, so the reads of one set never wait for the
+  // math of the other)
+  F f0, f1;
+  auto step = [&](int kb, F& mine, F& other) {
+    arrive_wait();  // B(kb): block kb + 1 is in LDS; everyone has finished reading block kb
+    if (kb + 1 < KB) read(kb + 1, other);
+    if (ST::kJ0 < 2 || !(half_last && kb == KB - 1)) math(mine);
+  };
+  arrive_wait();  // B(-1): block 0 is in LDS
+  read(0, f0);
+  int kb = 0;
+  for (; kb + 1 < KB; kb += 2) {
+    step(kb, f0, f1);
+    step(kb + 1, f1, f0);
   }
+  if (kb < KB) step(kb, f0, f1);
 }
 
-template <int BITS, int NP, int NTT, int LC, int LX, int W>
+template <int BITS, int NP, int NTT, int NC, int DC, int DX, int C>
 __device__ __forceinline__ void consumer(const KArgs& a, const char* cring, const char* xring,
                                          bool fast, f32x16 (&acc)[NP][NTT]) {
   if (fast)
-    consume<BITS, NP, NTT, LC, LX, W, true>(a, cring, xring, acc);
+    consume<BITS, NP, NTT, NC, DC, DX, C, true>(a, cring, xring, acc);
   else
-    consume<BITS, NP, NTT, LC, LX, W, false>(a, cring, xring, acc);
+    consume<BITS, NP, NTT, NC, DC, DX, C, false>(a, cring, xring, acc);
 }
 
-// Workgroup = 4 consumer waves (math) + 1 code producer + 1 activation producer.  LDS: the code
-// ring (LC + 1 stages), then the activation ring (LX + 1 stages); the reduction at the end
-// reuses the start of it.
-template <int BITS, int NP, int NTT, int LC, int LX, int EPI>
-__global__ __launch_bounds__(kThreads) void narrow_kernel(KArgs a) {
+// Workgroup = NC consumer waves (math) + 1 code producer + 1 activation producer.  LDS: the code
+// ring (DC stages), then the activation ring (DX stages); the reduction at the end reuses it.
+template <int BITS, int NP, int NTT, int NC, int DC, int DX, int EPI>
+__global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
   using CS = CodeStage<BITS, NP>;
   constexpr int BN = 32 * NTT, XB = BN * 256;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const cring = smem;
-  char* const xring = smem + (LC + 1) * CS::kBytes;
+  char* const xring = smem + DC * CS::kBytes;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ntiles = a.rows / 16;
@@ -218,18 +268,18 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(KArgs a) {
   // Producers start streaming at once; the consumers vote on the zero-points meanwhile: are all
   // of this workgroup's zero-points integers (1024 + z exact in fp16)?
   bool exact = true;
-  if (wave == kConsumers) {
+  if (wave == NC) {
 #pragma unroll
-    for (int j = 0; j < LC; ++j)
+    for (int j = 0; j < DC; ++j)
       load_codes<BITS, NP>(R, a, cring + j * CS::kBytes, pair0, ntiles, min(j, KB - 1), lane);
-  } else if (wave == kConsumers + 1) {
+  } else if (wave == NC + 1) {
 #pragma unroll
-    for (int j = 0; j < LX; ++j) load_x<BN>(R, a, xring + j * XB, voff, min(j, KB - 1));
+    for (int j = 0; j < DX; ++j) load_x<BN>(R, a, xring + j * XB, voff, min(j, KB - 1));
   } else {
     const int zbase = 2 * pair0 * KB * 64;  // bytes: zero-points of the workgroup's tiles
     const int zbytes = 2 * NP * KB * 64;
     const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f};
-    for (int off = threadIdx.x * 16; off < zbytes; off += 64 * kConsumers * 16) {
+    for (int off = threadIdx.x * 16; off < zbytes; off += 64 * NC * 16) {
       // past the last tile the range check reads zeros (integers)
       const u32x4 zz = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.z, zbase + off, 0, 0));
 #pragma unroll
@@ -245,27 +295,42 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(KArgs a) {
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[p][tt] = f32x16{};
 
-  if (wave == kConsumers) {
-    produce<LC, CS::kOps>(KB, [&](int st, int kb) {
+  if (wave == NC) {
+    produce<DC, CS::kOps>(KB, [&](int st, int kb) {
       load_codes<BITS, NP>(R, a, cring + st * CS::kBytes, pair0, ntiles, kb, lane);
     });
-  } else if (wave == kConsumers + 1) {
-    produce<LX, BN / 4>(KB, [&](int st, int kb) { load_x<BN>(R, a, xring + st * XB, voff, kb); });
+  } else if (wave == NC + 1) {
+    produce<DX, BN / 4>(KB, [&](int st, int kb) { load_x<BN>(R, a, xring + st * XB, voff, kb); });
   } else {
+#define W4_CONSUMER(C)                                                             \
+  case C:                                                                          \
+    consumer<BITS, NP, NTT, NC, DC, DX, C>(a, cring, xring, fast, acc); \
+    break;
     switch (wave) {
-      case 0: consumer<BITS, NP, NTT, LC, LX, 0>(a, cring, xring, fast, acc); break;
-      case 1: consumer<BITS, NP, NTT, LC, LX, 1>(a, cring, xring, fast, acc); break;
-      case 2: consumer<BITS, NP, NTT, LC, LX, 2>(a, cring, xring, fast, acc); break;
-      default: consumer<BITS, NP, NTT, LC, LX, 3>(a, cring, xring, fast, acc); break;
+      W4_CONSUMER(0)
+      W4_CONSUMER(1)
+      W4_CONSUMER(2)
+      W4_CONSUMER(3)
+      default:
+        if constexpr (NC == 8) {
+          switch (wave) {
+            W4_CONSUMER(4)
+            W4_CONSUMER(5)
+            W4_CONSUMER(6)
+            default: consumer<BITS, NP, NTT, NC, DC, DX, 7>(a, cring, xring, fast, acc); break;
+          }
+        }
+        break;
     }
+#undef W4_CONSUMER
   }
 
-  // Drain the producers' tail loads (they target LDS reused below), then add the four partial
+  // Drain the producers' tail loads (they target LDS reused below), then add the NC partial
   // sums in wave order.  red[w][p][tt][v][lane].
   wait_vmcnt<0>();
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
-  if (wave < kConsumers) {
+  if (wave < NC) {
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
@@ -274,22 +339,19 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(KArgs a) {
         for (int v = 0; v < 16; ++v) red[(((wave * NP + p) * NTT + tt) * 16 + v) * 64 + lane] = acc[p][tt][v];
   }
   __syncthreads();
-  if (wave >= kConsumers) return;
+  if (wave >= NC) return;
   auto sum = [&](int p, int tt, int v) {
     float s = red[(((0 * NP + p) * NTT + tt) * 16 + v) * 64 + lane];
-    s += red[(((1 * NP + p) * NTT + tt) * 16 + v) * 64 + lane];
-    s += red[(((2 * NP + p) * NTT + tt) * 16 + v) * 64 + lane];
-    s += red[(((3 * NP + p) * NTT + tt) * 16 + v) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < NC; ++w) s += red[(((w * NP + p) * NTT + tt) * 16 + v) * 64 + lane];
     return s;
   };
   const int h = lane >> 5;
   if constexpr (EPI == EPI_SWIGLU) {
-    // wave w: gate quad q = w % 2 (its up quad is registers 8 + 4q ..) of the items p*NTT+tt
-    // whose parity is w / 2
-#pragma unroll
-    for (int it = 0; it < NP * NTT; ++it) {
-      if ((it & 1) != (wave >> 1)) continue;
-      const int p = it / NTT, tt = it % NTT, q = wave & 1;
+    // (item, gate quad q) pairs, q in {0, 1}; the up quad of gate quad q is registers 8 + 4q ..
+    for (int idx = wave; idx < NP * NTT * 2; idx += NC) {
+      const int it = idx >> 1, q = idx & 1;
+      const int p = it / NTT, tt = it % NTT;
       const int pair = pair0 + p, t = 32 * tt + (lane & 31);
       if (t >= a.T || 2 * pair >= ntiles) continue;
       const f32x4 g = {sum(p, tt, 4 * q), sum(p, tt, 4 * q + 1), sum(p, tt, 4 * q + 2), sum(p, tt, 4 * q + 3)};
@@ -297,10 +359,9 @@ __global__ __launch_bounds__(kThreads) void narrow_kernel(KArgs a) {
       store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + 16 * pair + 8 * q + 4 * h, g, u);
     }
   } else {
-    // wave w: register quad q = w of every item (pair rows 8q + 4h + 0..3)
-    const int q = wave;
-#pragma unroll
-    for (int it = 0; it < NP * NTT; ++it) {
+    // (item, register quad q) pairs: pair rows 8q + 4h + 0..3
+    for (int idx = wave; idx < NP * NTT * 4; idx += NC) {
+      const int it = idx >> 2, q = idx & 3;
       const int p = it / NTT, tt = it % NTT;
       const int pair = pair0 + p, t = 32 * tt + (lane & 31);
       if (t >= a.T || 2 * pair >= ntiles) continue;
@@ -315,17 +376,18 @@ template <int BITS, int NP, int NTT, int EPI>
 hipError_t run(const KArgs& a, hipStream_t stream) {
   using CS = CodeStage<BITS, NP>;
   constexpr int BN = 32 * NTT;
-  constexpr int LX = 3;  // activation blocks in flight
-  constexpr int LCMAX = 63 / CS::kOps + 1;
-  constexpr int LC = LCMAX < 12 ? LCMAX : 12;  // code blocks in flight
+  constexpr int NC = 4;  // consumer waves
+  constexpr int DX = 4;  // activation stages
+  constexpr int DCMAX = 63 / CS::kOps + 1;
+  constexpr int DC = DCMAX < 12 ? DCMAX : 12;  // code stages
   const int ntiles = a.rows / 16;
   const int npairs = (ntiles + 1) / 2;
   const int grid = (npairs + NP - 1) / NP;
-  const size_t rings = (size_t)(LC + 1) * CS::kBytes + (size_t)(LX + 1) * BN * 256;
-  const size_t red = (size_t)kConsumers * NP * NTT * 16 * 64 * 4;
+  const size_t rings = (size_t)DC * CS::kBytes + (size_t)DX * BN * 256;
+  const size_t red = (size_t)NC * NP * NTT * 16 * 64 * 4;
   const size_t lds = rings > red ? rings : red;
-  hipLaunchKernelGGL((narrow_kernel<BITS, NP, NTT, LC, LX, EPI>), dim3(grid), dim3(kThreads), lds,
-                     stream, a);
+  hipLaunchKernelGGL((narrow_kernel<BITS, NP, NTT, NC, DC, DX, EPI>), dim3(grid),
+                     dim3(64 * (NC + 2)), lds, stream, a);
   return hipGetLastError();
 }
 

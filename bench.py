@@ -56,10 +56,19 @@ WORKLOADS = {
 }
 
 
-def kernel_source_sha() -> str:
+# Sources each measured kernel is built from (its own file, the headers it includes and the
+# route table that picks its instance): a traffic record is valid while these are unchanged.
+KERNEL_SOURCES = {
+    "stream_kernel": ["stream.hip", "device.h", "layout.h", "kernels.h", "api.hip"],
+    "narrow_kernel": ["narrow.hip", "tile32.h", "device.h", "layout.h", "kernels.h", "api.hip"],
+    "wide_kernel": ["wide.hip", "tile32.h", "device.h", "layout.h", "kernels.h", "api.hip"],
+}
+
+
+def kernel_source_sha(files) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4_groupwise_gemm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in sorted(files):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -68,13 +77,14 @@ def kernel_source_sha() -> str:
 
 def traffic_from_profiles(workload: str, T: int):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it still
-    describes the current kernel sources; else None."""
+    describes the current sources of the measured kernel; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_src_sha") != kernel_source_sha():
+    files = rec.get("kernel_sources")
+    if not files or rec.get("kernel_src_sha") != kernel_source_sha(files):
         return None
     v = rec.get("bytes_per_launch", {}).get(str(T))
     return None if v is None else float(v)
@@ -359,8 +369,14 @@ def traffic_summary(args) -> int:
     fscale, wscale = copy_bytes / (cf * 1024.0), copy_bytes / (cw * 1024.0)
     rd, wr = fetch * 1024.0 * fscale, write * 1024.0 * wscale
     T = args.widths
+    family = next((k for k in KERNEL_SOURCES if k in kname), None)
+    if family is None:
+        print(f"no source list for kernel {kname}", file=sys.stderr)
+        return 2
     rec = {
-        "workload": args.workload, "T": T, "kernel": kname, "kernel_src_sha": kernel_source_sha(),
+        "workload": args.workload, "T": T, "kernel": kname,
+        "kernel_sources": KERNEL_SOURCES[family],
+        "kernel_src_sha": kernel_source_sha(KERNEL_SOURCES[family]),
         "fetch_kib_per_dispatch": fetch, "write_kib_per_dispatch": write,
         "dispatches": {"fetch": nf, "write": nw, "copy_fetch": ncf, "copy_write": ncw},
         "copy_bytes": copy_bytes, "copy_fetch_kib": cf, "copy_write_kib": cw,

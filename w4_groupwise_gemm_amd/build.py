@@ -18,7 +18,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw4gemm.so")
 PROBE_LIB = os.path.join(HERE, "libw4probe.so")  # measurement support (read/copy/empty kernels)
 
-SOURCES = ["api.hip", "stream.hip", "narrow.hip", "wide.hip", "repack.cpp"]
+SOURCES = ["api.hip", "stream.hip", "narrow.hip", "splitk.hip", "wide.hip", "repack.cpp"]
 PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")

@@ -19,7 +19,7 @@
 
 namespace {
 
-enum RouteKind { KIND_GEMV = 0, KIND_STREAM = 1, KIND_NARROW = 2, KIND_WIDE = 3 };
+enum RouteKind { KIND_GEMV = 0, KIND_STREAM = 1, KIND_NARROW = 2, KIND_WIDE = 3, KIND_SPLITK = 4 };
 
 struct Route {
   const char* name;
@@ -34,9 +34,10 @@ const Route kRoutes[] = {
     {"mfma_narrow_t32", 1, 32, KIND_NARROW, 32},
     {"mfma_narrow_t64", 1, 64, KIND_NARROW, 64},
     {"mfma_wide", 1, INT_MAX, KIND_WIDE, 0},
+    {"mfma_splitk_t32", 1, 32, KIND_SPLITK, 32},
 };
 constexpr int kNumRoutes = sizeof(kRoutes) / sizeof(kRoutes[0]);
-enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4 };
+enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5 };
 
 constexpr int kMaxDim = 1 << 24;
 
@@ -144,6 +145,7 @@ int launch_route(int route, int op, const void* x, const void* w, const void* s,
     case KIND_STREAM: e = w4::launch_stream16(bits, epi, a, st); break;
     case KIND_NARROW: e = w4::launch_narrow(R.tn, bits, epi, a, st); break;
     case KIND_WIDE: e = w4::launch_wide(bits, epi, a, st); break;
+    case KIND_SPLITK: e = w4::launch_splitk(bits, epi, a, st); break;
     default: return W4_ERR_DOMAIN;
   }
   return e == hipSuccess ? W4_OK : W4_ERR_LAUNCH;

@@ -26,5 +26,6 @@ hipError_t launch_gemv(int bits, int epi, const KArgs& a, hipStream_t stream);  
 hipError_t launch_stream16(int bits, int epi, const KArgs& a, hipStream_t stream);  // T <= 16
 hipError_t launch_narrow(int tn, int bits, int epi, const KArgs& a, hipStream_t stream);  // T <= tn
 hipError_t launch_wide(int bits, int epi, const KArgs& a, hipStream_t stream);    // any T
+hipError_t launch_splitk(int bits, int epi, const KArgs& a, hipStream_t stream);  // T <= 32
 
 }  // namespace w4

@@ -111,6 +111,9 @@ def main() -> int:
                          "(subdirs fetch, write, copy_fetch, copy_write) into the traffic record")
     ap.add_argument("--kernel-match", default=None,
                     help="substring of the measured kernel's name (with --traffic-summary)")
+    ap.add_argument("--route-sweep", action="store_true",
+                    help="time every route whose T domain holds each width (graph replays of "
+                         "back-to-back launches over the cold copies); prints one JSON line")
     ap.add_argument("--copy-mb", type=float, default=256.0,
                     help="--probe-mb of the copy runs (with --traffic-summary)")
     args = ap.parse_args()
@@ -131,12 +134,15 @@ def main() -> int:
         return run_probe(args)
 
     cfg_name, widths, opname = WORKLOADS[args.workload]
+    all_widths = widths
     if args.widths:
         widths = tuple(int(v) for v in args.widths.split(","))
+        # X is drawn once at the largest width (so a token's row is the same at every width)
+        all_widths = tuple(sorted(set(all_widths) | set(widths)))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating {cfg_name}", file=sys.stderr, flush=True)
-    wl = make_workload(cfg_name)
+    wl = make_workload(cfg_name, Ts=all_widths)
     bits = wl.weights[0].bits
     K = wl.weights[0].K
     if opname == "swiglu":
@@ -175,6 +181,10 @@ def main() -> int:
         if op == w4.OP_ADD:
             return w4.linear_add(xs[T], pw, res[T], out=outs[T])
         return w4.linear(xs[T], pw, out=outs[T])
+
+    if args.route_sweep:
+        return route_sweep(args, w4, torch, widths, op, pws, xs, res, outs, copies, wstream_alg,
+                           N, K, rows, bits)
 
     # ---- outputs of the first launch at each width, kept for the parity check of the
     # cpu_baseline leg (sampled output columns against the fp64 oracle, same run)
@@ -292,6 +302,49 @@ def main() -> int:
     }
     print(json.dumps(line))
     return 1 if parity_ok is False else 0
+
+
+def route_sweep(args, w4, torch, widths, op, pws, xs, res, outs, copies, wstream_alg, N, K, rows,
+                bits) -> int:
+    """Per-launch time of every route at every width (the data the route boundaries are chosen
+    from): graph replays of `copies` back-to-back launches, HIP events, median of 5."""
+    stream = torch.cuda.current_stream()
+    table = {}
+    for T in widths:
+        for rid in range(w4.route_count()):
+            lo, hi = w4.route_domain(rid)
+            if not lo <= T <= hi:
+                continue
+            name = w4.route_name(rid)
+
+            def one(c, T=T, rid=rid):
+                w4.linear_route(rid, op, xs[T], pws[c], residual=res.get(T), out=outs[T])
+
+            one(0)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in range(copies):
+                    one(c)
+            g.replay()
+            torch.cuda.synchronize()
+            samples = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                samples.append(e0.elapsed_time(e1) * 1e3 / copies)
+            us = float(np.median(samples))
+            table.setdefault(str(T), {})[name] = us
+            print(f"[sweep] {args.workload} T={T:5d} {name:18s} {us:9.2f} us  "
+                  f"{wstream_alg / us / 1e3:7.0f} GB/s  {2.0 * T * rows * K / us / 1e6:7.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+    best = {T: min(r, key=r.get) for T, r in table.items()}
+    print(json.dumps({"route_sweep": args.workload, "N": N, "K": K, "bits": bits,
+                      "cold_copies": copies, "us": table, "fastest": best}))
+    return 0
 
 
 def run_probe(args) -> int:

@@ -108,12 +108,17 @@ int device_check() {
   return v == 1 ? W4_OK : W4_ERR_DEVICE;
 }
 
+// Boundaries from route sweeps on this chip (every route timed at the same T, cold weights, at
+// the decode, batched-decode, SwiGLU-pair and 5120-row prefill shapes): the streaming kernel
+// wins up to 6 tokens, the split-K kernel from 8 to 12, the warp-specialised narrow kernels from
+// 16 to 64 (16: 16.2 vs 16.8 us at 11264 rows; tied on the SwiGLU pair).
 int pick_route(int op, int bits, int T, int N, int K) {
   (void)op;
   (void)bits;
   (void)N;
   (void)K;
-  if (T <= 16) return R_N16;
+  if (T <= 6) return R_N16;
+  if (T <= 12) return R_SPLITK;
   if (T <= 32) return R_N32;
   if (T <= 64) return R_N64;
   return R_WIDE;

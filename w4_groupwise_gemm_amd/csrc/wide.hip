@@ -117,9 +117,9 @@ __device__ __forceinline__ void deq_a(const PairCodes<BITS>& cur, const ShareCod
 }
 
 // Step I of the software pipeline: the matrix-core steps of step I run while the B fragments of
-// step I + 1 are read and its A fragments dequantised.  The schedule interleaves one
-// matrix-core step with a few vector ops and one LDS read, so that with one wave per SIMD the
-// vector work issues in the shadow of the matrix cores.
+// step I + 1 are read and its A fragments dequantised.  The instruction order inside a step is
+// left to the compiler (measured: forcing one matrix-core step / one LDS read / a few vector ops
+// in turn was 4-6% slower); the barrier at the end keeps steps from mixing.
 template <int BITS, int NP, int NTT, int W, int I, bool FAST>
 __device__ __forceinline__ void wide_step(const PairCodes<BITS>& cur, const ShareCodes<BITS>& sh,
                                           const char* xs, int bsw, uint32_t magic,
@@ -137,15 +137,6 @@ __device__ __forceinline__ void wide_step(const PairCodes<BITS>& cur, const Shar
   if constexpr (SH) {
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) accs[tt] = mfma32(A4cur, Bcur[tt], accs[tt]);
-  }
-  constexpr int M = NTT * (SH ? 2 : 1);
-  constexpr int V = (I + 1 < 8) ? (BITS == 5 ? 20 : 14) * (share_step<NP, W, I + 1>() ? 2 : 1) : 0;
-  constexpr int VPER = (V + M - 1) / M;
-#pragma unroll
-  for (int i = 0; i < M; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix-core step
-    if (i < NTT) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    __builtin_amdgcn_sched_group_barrier(0x002, VPER, 0);  // vector ops
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -341,11 +332,11 @@ hipError_t pick(const KArgs& a, hipStream_t stream) {
   // 160-row workgroups (5 pairs) divide the 5120-row projections into 32 row blocks; the
   // SwiGLU pair layout (gate, up) keeps every 32-row pair inside one output tile either way.
   const bool five = (ntiles % 10 == 0);
-  const int nrb = five ? ntiles / 10 : (ntiles + 7) / 8;
-  // the 256-token tile when it still gives every compute unit two workgroups, else 128
-  const bool wide = (long)nrb * ((a.T + 255) / 256) >= 512;
-  if (five) return wide ? run<BITS, 5, 8, EPI>(a, stream) : run<BITS, 5, 4, EPI>(a, stream);
-  return wide ? run<BITS, 4, 8, EPI>(a, stream) : run<BITS, 4, 4, EPI>(a, stream);
+  // 128-token tiles, two workgroups per compute unit (measured against 256-token tiles with
+  // one workgroup per compute unit: 290 vs 296 us at 5120 x 6144, T = 4096; the narrower tile
+  // re-dequantises each weight block twice as often but lets two waves share each SIMD)
+  if (five) return run<BITS, 5, 4, EPI>(a, stream);
+  return run<BITS, 4, 4, EPI>(a, stream);
 }
 
 template <int BITS>

@@ -102,6 +102,10 @@ def main() -> int:
     ap.add_argument("--probe", choices=["copy", "read"], default=None,
                     help="run only the plain copy/read kernel of libw4probe.so (counter reference)")
     ap.add_argument("--probe-mb", type=float, default=256.0)
+    ap.add_argument("--probe-cold", action="store_true",
+                    help="read probe over rotated copies (--cold-bytes GiB), graph-replayed "
+                         "back to back like the GEMM launches: the cold-read ceiling at that size")
+    ap.add_argument("--probe-grid", type=int, default=2048, help="workgroups of the probe kernels")
     ap.add_argument("--widths", default=None,
                     help="comma list of T overriding the workload's widths (counter runs)")
     ap.add_argument("--no-graph", action="store_true",
@@ -218,8 +222,13 @@ def main() -> int:
         return g
 
     stream = torch.cuda.current_stream()
-    g_warm = capture([(T, s % copies) for s in range(max(1, args.warmup)) for T in widths])
-    g_steps = capture([(T, s % copies) for s in range(args.steps) for T in widths])
+    # every launch of a step reads a weight copy that no launch has touched since the other
+    # copies went through (a copy is never reused inside a step: no Infinity Cache hits)
+    def rotation(nsteps):
+        return [(T, (s * len(widths) + i) % copies) for s in range(nsteps) for i, T in enumerate(widths)]
+
+    g_warm = capture(rotation(max(1, args.warmup)))
+    g_steps = capture(rotation(args.steps))
     g_width = {T: capture([(T, c) for c in range(copies)]) for T in widths}
     g_warm.replay()
     for g in g_width.values():
@@ -349,7 +358,10 @@ def route_sweep(args, w4, torch, widths, op, pws, xs, res, outs, copies, wstream
 
 def run_probe(args) -> int:
     """Plain copy (or read) kernel over a buffer of known size: the reference for scaling the
-    FETCH_SIZE / WRITE_SIZE counters, and the achievable HBM read rate."""
+    FETCH_SIZE / WRITE_SIZE counters, and the achievable HBM read rate.  With --probe-cold the
+    read kernel walks rotated copies (each launch reads a buffer that no launch has touched
+    since the others went through), timed like the GEMM launches: HIP events around graph
+    replays of back-to-back launches."""
     import ctypes
     import torch
     P = ctypes.CDLL(os.path.join(ROOT, "w4_groupwise_gemm_amd", "libw4probe.so"))
@@ -357,18 +369,51 @@ def run_probe(args) -> int:
     P.w4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     nbytes = int(args.probe_mb * 1e6) // 4096 * 4096
     dev = torch.device("cuda:0")
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    dst = torch.empty(nbytes if args.probe == "copy" else 16, dtype=torch.uint8, device=dev)
+    grid = args.probe_grid
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)
+    if args.probe_cold:
+        if args.probe != "read":
+            raise SystemExit("--probe-cold applies to --probe read")
+        copies = max(2, int(np.ceil(args.cold_bytes * (1 << 30) / nbytes)))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
+        sink = torch.empty(16, dtype=torch.uint8, device=dev)
+
+        def launch_all():
+            cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)  # the capture stream
+            for b in bufs:
+                if P.w4probe_read(b.data_ptr(), nbytes, sink.data_ptr(), grid, cs) != 0:
+                    raise RuntimeError("probe launch failed")
+
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            launch_all()
+        stream = torch.cuda.current_stream()
+        for _ in range(max(1, args.warmup)):
+            g.replay()
+        torch.cuda.synchronize()
+        samples = []
+        for _ in range(max(1, args.steps)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            samples.append(e0.elapsed_time(e1) * 1e3 / copies)
+        us = float(np.median(samples))
+        print(json.dumps({"probe": "read_cold", "bytes_read": nbytes, "copies": copies, "grid": grid,
+                          "us_median": us, "GBs": nbytes / us / 1e3}))
+        return 0
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes if args.probe == "copy" else 16, dtype=torch.uint8, device=dev)
     times = []
     for i in range(args.warmup + args.steps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         if args.probe == "copy":
-            rc = P.w4probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, 2048, sh)
+            rc = P.w4probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, grid, sh)
         else:
-            rc = P.w4probe_read(src.data_ptr(), nbytes, dst.data_ptr(), 2048, sh)
+            rc = P.w4probe_read(src.data_ptr(), nbytes, dst.data_ptr(), grid, sh)
         e1.record(stream)
         if rc != 0:
             raise RuntimeError(f"probe launch failed: {rc}")

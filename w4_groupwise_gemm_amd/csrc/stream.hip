@@ -8,9 +8,12 @@
 // gfx950 design.  At these widths the kernel is an HBM stream with a dequantisation tax, so
 // everything is arranged around keeping enough 16-byte code loads in flight and keeping the
 // vector ALU work per packed word minimal:
-//  * a workgroup owns RT 16-row tiles; its NW waves split K into NW contiguous block ranges,
-//    so each code byte is loaded exactly once, into the lane that feeds it to the math;
-//  * each wave keeps a ring of D k-blocks of loads in flight ahead of the math;
+//  * a workgroup owns RT 16-row tiles; its NW waves split K, wave w taking k-blocks w, w + NW,
+//    w + 2 NW, ... (at any moment the workgroup streams NW adjacent blocks of a tile), so each
+//    code byte is loaded exactly once, into the lane that feeds it to the math;
+//  * each wave keeps a ring of D k-blocks of loads in flight ahead of the math (with one row
+//    tile, all of its blocks: the stream never waits for the math); code loads are
+//    non-temporal (each byte is read once per call);
 //  * for T <= 4 the wave's activation slice (T rows of its K range) is loaded first and
 //    parked in a wave-private LDS region, so activation reads never wait behind code loads in
 //    the in-order load counter and no barrier is needed inside the loop; for larger T the
@@ -104,7 +107,8 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = a.rows / 16;
   const int tile0 = blockIdx.x * RT;
-  const int kbw0 = (a.KB * wave) / NW, kbw1 = (a.KB * (wave + 1)) / NW;
+  // local block index c of this wave is k-block wave + NW * c; nbw of them
+  const int nbw = wave < a.KB ? (a.KB - wave + NW - 1) / NW : 0;
   const int T = a.T;
   const int tr = min(r, T - 1);
   const uint32_t magic = vgpr_const(0x64006400u);
@@ -120,14 +124,14 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
   }
 
   Ring<BITS, RT, KPW, XL> R;
-  // Without LOOP the launcher guarantees at most one chunk per wave (kbw1 - kbw0 <= KPW): a
-  // runtime loop around the unrolled ring costs about a third more registers.  A wave whose
-  // K range is empty (K shorter than NW k-blocks) skips the body entirely: its activation
-  // slice would otherwise be addressed from chunk -1.
-  for (int cb = kbw0; LOOP ? cb < kbw1 : (cb == kbw0 && cb < kbw1); cb += KPW) {
-    const int nb = min(KPW, kbw1 - cb);
+  // Without LOOP the launcher guarantees at most one chunk per wave (nbw <= KPW): a runtime
+  // loop around the unrolled ring costs about a third more registers.  A wave without blocks
+  // (K shorter than NW k-blocks) skips the body entirely.
+  for (int cb = 0; LOOP ? cb < nbw : (cb == 0 && cb < nbw); cb += KPW) {
+    const int nb = min(KPW, nbw - cb);
 
-    // activation slice of this chunk (T <= 4 rows), loaded before any code of the chunk
+    // activation slice of this chunk (T <= 4 rows, nb k-blocks of 128 columns, parked in LDS
+    // back to back), loaded before any code of the chunk
     constexpr int XCH = (KPW * 16 + 63) / 64;  // 16-byte chunks per lane per token row
     u32x4 xr[XL ? 4 : 1][XL ? XCH : 1];
     if constexpr (XL == 1) {
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
 #pragma unroll
           for (int i = 0; i < XCH; ++i) {
             const int c = min(lane + 64 * i, cpt - 1);
-            const int kk = min(cb * 128 + c * 8, a.K - 8);
+            const int kk = min((wave + NW * (cb + (c >> 4))) * 128 + (c & 15) * 8, a.K - 8);
             xr[t][i] = *reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.K + kk);
           }
         }
@@ -146,14 +150,14 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
     }
 
     auto issue = [&](int i) {
-      const int kb = cb + i;
+      const int kb = wave + NW * (cb + i);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int tile = min(tile0 + rt, ntiles - 1);
         const size_t bi = (size_t)tile * a.KB + kb;
-        R.cw[i][rt] = *reinterpret_cast<const u32x4*>(a.w + bi * BLK + lane * 16);
+        R.cw[i][rt] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.w + bi * BLK + lane * 16));
         if constexpr (BITS == 5)
-          R.hw[i][rt] = *reinterpret_cast<const uint32_t*>(a.w + bi * BLK + 1024 + lane * 4);
+          R.hw[i][rt] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.w + bi * BLK + 1024 + lane * 4));
         else
           R.hw[i][rt] = 0;
         R.sp[i][rt] = a.sc[bi * 16 + r];
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
     for (int i = 0; i < KPW; ++i) {
       if (i + D < nb) issue(i + D);
       if (i < nb) {
-        const int kb = cb + i;
+        const int kb = wave + NW * (cb + i);
         const bool half_block = (kb * 128 + 64 >= a.K);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -312,11 +316,14 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
 }
 
 constexpr int kNW = 8;  // waves per workgroup (K split)
-// Ring depth (k-blocks of loads in flight ahead of the math): 3 for one row tile per workgroup;
-// 2 for two, where the smaller register footprint buys more resident waves (measured: SwiGLU
-// pair, 34816 packed rows, T = 1: 26.5 us against 30.0 us with 3).
-template <int RT>
-constexpr int ring_depth() { return RT >= 2 ? 2 : 3; }
+// Ring depth (k-blocks of loads in flight ahead of the math).  One row tile with the
+// activation slice in LDS: 5, every block of a 5120-column wave in flight at once (decode
+// 12288 x 5120, T = 1: 11.1 us with 3, 10.6 us with 5).  Activation fragments in the ring
+// (T > 4): 3, since each stage then costs 16 more registers.  Two row tiles: 2, where the
+// smaller register footprint buys more resident waves (SwiGLU pair, 34816 packed rows, T = 1:
+// 26.5 us against 30.0 us with 3).
+template <int RT, int XL>
+constexpr int ring_depth() { return RT >= 2 ? 2 : (XL ? 5 : 3); }
 
 template <int BITS, int MODE, int RT, int XL, int EPI, int KPW, bool LOOP>
 hipError_t run_k(const KArgs& a, hipStream_t stream) {
@@ -327,7 +334,7 @@ hipError_t run_k(const KArgs& a, hipStream_t stream) {
   size_t lds = XL ? (size_t)kNW * 4 * xstride * 2 : 0;
   const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * 64 * 16 : (size_t)kNW * RT * 64 * 4;
   if (red > lds) lds = red;
-  hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, ring_depth<RT>(), XL, EPI, LOOP>),
+  hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, ring_depth<RT, XL>(), XL, EPI, LOOP>),
                      dim3((ntiles + RT - 1) / RT), dim3(kNW * 64), lds, stream, a, xstride);
   return hipGetLastError();
 }

@@ -26,6 +26,8 @@
 //  * token rows beyond T are clamped to row T-1 instead of masked: those output columns are
 //    never stored, so the loads need no exec masking;
 //  * the NW partial sums are combined in LDS in a fixed order (bitwise deterministic).
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -149,8 +151,11 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
       }
     }
 
+    // Loads of local block i.  The first D blocks are issued unconditionally (a wave with
+    // fewer blocks re-reads its last one), so that the compiler counts the loads in flight
+    // exactly and waits for each block alone rather than for the whole ring.
     auto issue = [&](int i) {
-      const int kb = wave + NW * (cb + i);
+      const int kb = wave + NW * (cb + min(i, nb - 1));
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const int tile = min(tile0 + rt, ntiles - 1);
@@ -173,9 +178,9 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
                            : *reinterpret_cast<const u32x4*>(xrow + 64 * (j >> 1) + 8 * (j & 1));
       }
     };
+    static_assert(D <= KPW, "ring deeper than the chunk");
 #pragma unroll
-    for (int i = 0; i < D; ++i)
-      if (i < nb) issue(i);
+    for (int i = 0; i < D; ++i) issue(i);
 
     if constexpr (XL == 1) {
       const int cpt = nb * 16;
@@ -196,10 +201,22 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
 
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
-      if (i + D < nb) issue(i + D);
+      if (i + D < KPW && i + D < nb) issue(i + D);
       if (i < nb) {
         const int kb = wave + NW * (cb + i);
         const bool half_block = (kb * 128 + 64 >= a.K);
+        // activation fragments of the block's four 32-k steps, read before the dequantisation
+        // so that the LDS latency hides behind it (a half-empty last block skips steps 2, 3)
+        f16x8 Bf[4];
+        if constexpr (MODE == MODE_MFMA) {
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            if constexpr (XL == 1)
+              Bf[J] = *reinterpret_cast<const f16x8*>(xs + tr * xstride + i * 128 + 64 * (J >> 1) + 16 * g + 8 * (J & 1));
+            else
+              Bf[J] = __builtin_bit_cast(f16x8, R.xb[i][J]);
+          }
+        }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
           // exact wave-uniform test: are both zero-points of this block integers?
@@ -209,42 +226,67 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
           const bool exact = __builtin_bit_cast(uint32_t, (-nb0) - c1024) == R.zp[i][rt];
           const bool fast = __ballot(exact) == ~0ull;
           const f16x2 nb1 = -(z2p + c64);
-#define W4_STREAM_J(J)                                                                        \
-  if (!(half_block && (J) >= 2)) {                                                            \
-    const f16x2 s2 = splat<((J) >> 1)>(R.sp[i][rt]);                                          \
-    f16x2 wv[4];                                                                              \
-    if (fast)                                                                                 \
-      weights<BITS, J, true>(R.cw[i][rt][J], R.hw[i][rt], magic, f16x2{},                     \
-                             splat<((J) >> 1)>(__builtin_bit_cast(uint32_t, nb0)),            \
-                             splat<((J) >> 1)>(__builtin_bit_cast(uint32_t, nb1)), s2, wv);   \
-    else                                                                                      \
-      weights<BITS, J, false>(R.cw[i][rt][J], R.hw[i][rt], magic,                             \
-                              splat<((J) >> 1)>(R.zp[i][rt]), f16x2{}, f16x2{}, s2, wv);      \
-    const int koff = i * 128 + 64 * ((J) >> 1) + 16 * g + 8 * ((J) & 1);                      \
-    if constexpr (MODE == MODE_MFMA) {                                                        \
-      f16x8 B;                                                                                \
-      if constexpr (XL == 1)                                                                  \
-        B = *reinterpret_cast<const f16x8*>(xs + tr * xstride + koff);                        \
-      else                                                                                    \
-        B = __builtin_bit_cast(f16x8, R.xb[i][J]);                                            \
-      acc[rt] = mfma16(cat8(wv[0], wv[1], wv[2], wv[3]), B, acc[rt]);                         \
-    } else {                                                                                  \
-      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
-        if (t < T) {                                                                          \
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + t * xstride + koff);         \
-          float v = accd[rt][t];                                                              \
-          _Pragma("unroll") for (int p = 0; p < 4; ++p)                                       \
-              v = __builtin_amdgcn_fdot2(wv[p], as_h2(xv[p]), v, false);                      \
-          accd[rt][t] = v;                                                                    \
-        }                                                                                     \
-      }                                                                                       \
-    }                                                                                         \
-  }
-          W4_STREAM_J(0)
-          W4_STREAM_J(1)
-          W4_STREAM_J(2)
-          W4_STREAM_J(3)
-#undef W4_STREAM_J
+          // fp16 weights of dword J (8 k slots of the lane's row) as four pairs
+          auto wts = [&](auto jc, bool is_fast, f16x2 (&wv)[4]) {
+            constexpr int J = decltype(jc)::value;
+            const f16x2 s2 = splat<(J >> 1)>(R.sp[i][rt]);
+            if (is_fast)
+              weights<BITS, J, true>(R.cw[i][rt][J], R.hw[i][rt], magic, f16x2{},
+                                     splat<(J >> 1)>(__builtin_bit_cast(uint32_t, nb0)),
+                                     splat<(J >> 1)>(__builtin_bit_cast(uint32_t, nb1)), s2, wv);
+            else
+              weights<BITS, J, false>(R.cw[i][rt][J], R.hw[i][rt], magic,
+                                      splat<(J >> 1)>(R.zp[i][rt]), f16x2{}, f16x2{}, s2, wv);
+          };
+          if constexpr (MODE == MODE_MFMA) {
+            // all four A fragments first (one uniform branch per block), then the four steps
+            f16x8 A[4];
+            auto all_a = [&](bool is_fast) {
+              f16x2 wv[4];
+              wts(std::integral_constant<int, 0>{}, is_fast, wv);
+              A[0] = cat8(wv[0], wv[1], wv[2], wv[3]);
+              wts(std::integral_constant<int, 1>{}, is_fast, wv);
+              A[1] = cat8(wv[0], wv[1], wv[2], wv[3]);
+              if (!half_block) {
+                wts(std::integral_constant<int, 2>{}, is_fast, wv);
+                A[2] = cat8(wv[0], wv[1], wv[2], wv[3]);
+                wts(std::integral_constant<int, 3>{}, is_fast, wv);
+                A[3] = cat8(wv[0], wv[1], wv[2], wv[3]);
+              }
+            };
+            if (fast)
+              all_a(true);
+            else
+              all_a(false);
+            acc[rt] = mfma16(A[0], Bf[0], acc[rt]);
+            acc[rt] = mfma16(A[1], Bf[1], acc[rt]);
+            if (!half_block) {
+              acc[rt] = mfma16(A[2], Bf[2], acc[rt]);
+              acc[rt] = mfma16(A[3], Bf[3], acc[rt]);
+            }
+          } else {
+            auto dot_j = [&](auto jc) {
+              constexpr int J = decltype(jc)::value;
+              if (half_block && J >= 2) return;
+              f16x2 wv[4];
+              wts(jc, fast, wv);
+              const int koff = i * 128 + 64 * (J >> 1) + 16 * g + 8 * (J & 1);
+#pragma unroll
+              for (int t = 0; t < 4; ++t) {
+                if (t < T) {
+                  const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + t * xstride + koff);
+                  float v = accd[rt][t];
+#pragma unroll
+                  for (int p = 0; p < 4; ++p) v = __builtin_amdgcn_fdot2(wv[p], as_h2(xv[p]), v, false);
+                  accd[rt][t] = v;
+                }
+              }
+            };
+            dot_j(std::integral_constant<int, 0>{});
+            dot_j(std::integral_constant<int, 1>{});
+            dot_j(std::integral_constant<int, 2>{});
+            dot_j(std::integral_constant<int, 3>{});
+          }
         }
       }
     }
@@ -321,9 +363,12 @@ constexpr int kNW = 8;  // waves per workgroup (K split)
 // 12288 x 5120, T = 1: 11.1 us with 3, 10.6 us with 5).  Activation fragments in the ring
 // (T > 4): 3, since each stage then costs 16 more registers.  Two row tiles: 2, where the
 // smaller register footprint buys more resident waves (SwiGLU pair, 34816 packed rows, T = 1:
-// 26.5 us against 30.0 us with 3).
-template <int RT, int XL>
-constexpr int ring_depth() { return RT >= 2 ? 2 : (XL ? 5 : 3); }
+// 26.5 us against 30.0 us with 3).  Never deeper than the chunk.
+template <int RT, int XL, int KPW>
+constexpr int ring_depth() {
+  constexpr int d = RT >= 2 ? 2 : (XL ? 5 : 3);
+  return d < KPW ? d : KPW;
+}
 
 template <int BITS, int MODE, int RT, int XL, int EPI, int KPW, bool LOOP>
 hipError_t run_k(const KArgs& a, hipStream_t stream) {
@@ -334,16 +379,21 @@ hipError_t run_k(const KArgs& a, hipStream_t stream) {
   size_t lds = XL ? (size_t)kNW * 4 * xstride * 2 : 0;
   const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * 64 * 16 : (size_t)kNW * RT * 64 * 4;
   if (red > lds) lds = red;
-  hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, ring_depth<RT, XL>(), XL, EPI, LOOP>),
+  hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, ring_depth<RT, XL, KPW>(), XL, EPI, LOOP>),
                      dim3((ntiles + RT - 1) / RT), dim3(kNW * 64), lds, stream, a, xstride);
   return hipGetLastError();
 }
 
-// k-blocks per wave: one unrolled chunk for K <= 16384, a chunk loop beyond.
+// k-blocks per wave: one unrolled chunk for K <= 16384 (exactly the wave's block count up to
+// 5, so that no ring slot is a re-read), a chunk loop beyond.
 template <int BITS, int MODE, int RT, int XL, int EPI>
 hipError_t run(const KArgs& a, hipStream_t stream) {
   const int nbw = (a.KB + kNW - 1) / kNW;
-  if (nbw <= 5) return run_k<BITS, MODE, RT, XL, EPI, 5, false>(a, stream);
+  if (nbw <= 1) return run_k<BITS, MODE, RT, XL, EPI, 1, false>(a, stream);
+  if (nbw == 2) return run_k<BITS, MODE, RT, XL, EPI, 2, false>(a, stream);
+  if (nbw == 3) return run_k<BITS, MODE, RT, XL, EPI, 3, false>(a, stream);
+  if (nbw == 4) return run_k<BITS, MODE, RT, XL, EPI, 4, false>(a, stream);
+  if (nbw == 5) return run_k<BITS, MODE, RT, XL, EPI, 5, false>(a, stream);
   if (nbw <= 8) return run_k<BITS, MODE, RT, XL, EPI, 8, false>(a, stream);
   if (nbw <= 16) return run_k<BITS, MODE, RT, XL, EPI, 16, false>(a, stream);
   return run_k<BITS, MODE, RT, XL, EPI, 8, true>(a, stream);

@@ -110,15 +110,16 @@ int device_check() {
 
 // Boundaries from route sweeps on this chip (every route timed at the same T, cold weights, at
 // the decode, batched-decode, SwiGLU-pair and 5120-row prefill shapes): the streaming kernel
-// wins up to 6 tokens, the split-K kernel from 8 to 12, the warp-specialised narrow kernels from
-// 16 to 64 (16: 16.2 vs 16.8 us at 11264 rows; tied on the SwiGLU pair).
+// wins up to 10 tokens (SwiGLU pair: up to 16), the split-K kernel from 12 to 16 (16: 15.9 vs
+// 16.3 us at 11264 rows), the warp-specialised narrow kernels from 20 to 64.
 int pick_route(int op, int bits, int T, int N, int K) {
-  (void)op;
   (void)bits;
   (void)N;
   (void)K;
-  if (T <= 6) return R_N16;
-  if (T <= 12) return R_SPLITK;
+  // the SwiGLU pair streams two row tiles per workgroup, which keeps the streaming route ahead
+  // up to its 16-token limit
+  if (T <= 10 || (op == W4_OP_SWIGLU && T <= 16)) return R_N16;
+  if (T <= 18) return R_SPLITK;
   if (T <= 32) return R_N32;
   if (T <= 64) return R_N64;
   return R_WIDE;

@@ -117,12 +117,14 @@ __global__ __launch_bounds__(NW * 64) void splitk_kernel(KArgs a) {
   for (int c0 = kb0; LOOP ? c0 < kb1 : c0 == kb0; c0 += KPW) {
     const int nb = min(KPW, kb1 - c0);
     Blk<NP> ring[KPW];
+    // the first D blocks unconditionally (a wave with fewer blocks re-reads its last one): the
+    // compiler then counts the loads in flight exactly and waits for one block at a time
+    static_assert(D <= KPW, "ring deeper than the chunk");
 #pragma unroll
-    for (int i = 0; i < D; ++i)
-      if (i < nb) issue<BITS, NP>(ring[i], R, a, m, pair0, ntiles, c0 + i, xoff);
+    for (int i = 0; i < D; ++i) issue<BITS, NP>(ring[i], R, a, m, pair0, ntiles, c0 + min(i, nb - 1), xoff);
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
-      if (i + D < nb) issue<BITS, NP>(ring[i + D], R, a, m, pair0, ntiles, c0 + i + D, xoff);
+      if (i + D < KPW && i + D < nb) issue<BITS, NP>(ring[i + D], R, a, m, pair0, ntiles, c0 + i + D, xoff);
       if (i < nb) {
         // exact wave-uniform test: are all zero-points of this block integers (1024 + z exact)?
         bool exact = true;

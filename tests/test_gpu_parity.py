@@ -26,6 +26,7 @@ ROUTE_TS = {
     "mfma_narrow_t64": (33, 40, 64),
     "mfma_wide": (1, 65, 129, 300),
     "mfma_splitk_t32": (1, 7, 17, 32),
+    "mfma_narrow_tiled": (1, 33, 65, 129, 200),
 }
 
 

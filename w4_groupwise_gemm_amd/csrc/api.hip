@@ -35,9 +35,10 @@ const Route kRoutes[] = {
     {"mfma_narrow_t64", 1, 64, KIND_NARROW, 64},
     {"mfma_wide", 1, INT_MAX, KIND_WIDE, 0},
     {"mfma_splitk_t32", 1, 32, KIND_SPLITK, 32},
+    {"mfma_narrow_tiled", 1, INT_MAX, KIND_NARROW, 64},
 };
 constexpr int kNumRoutes = sizeof(kRoutes) / sizeof(kRoutes[0]);
-enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5 };
+enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5, R_NTILED = 6 };
 
 constexpr int kMaxDim = 1 << 24;
 
@@ -111,10 +112,10 @@ int device_check() {
 // Boundaries from route sweeps on this chip (every route timed at the same T, cold weights, at
 // the decode, batched-decode, SwiGLU-pair and 5120-row prefill shapes): the streaming kernel
 // wins up to 10 tokens (SwiGLU pair: up to 16), the split-K kernel from 12 to 16 (16: 15.9 vs
-// 16.3 us at 11264 rows), the warp-specialised narrow kernels from 20 to 64.
+// 16.3 us at 11264 rows), the warp-specialised narrow kernels from 20 to 64 and, token-tiled,
+// beyond that while the wide kernel's grid is small; the wide kernel above.
 int pick_route(int op, int bits, int T, int N, int K) {
   (void)bits;
-  (void)N;
   (void)K;
   // the SwiGLU pair streams two row tiles per workgroup, which keeps the streaming route ahead
   // up to its 16-token limit
@@ -122,6 +123,12 @@ int pick_route(int op, int bits, int T, int N, int K) {
   if (T <= 18) return R_SPLITK;
   if (T <= 32) return R_N32;
   if (T <= 64) return R_N64;
+  // Above 64 tokens the wide kernel's workgroups (about 128 rows x 128 tokens each) leave most
+  // compute units idle until there are about 128 of them; below that the narrow kernel run as
+  // side-by-side 64-token blocks is faster (5120 rows: 34 vs 73 us at T = 128, 67 vs 73 at 384,
+  // 81 vs 74 at 512; 11264 rows: 36 vs 46 at 128, 54 vs 47 at 256).
+  const long long rows = op == W4_OP_SWIGLU ? 2LL * N : (long long)N;
+  if ((rows + 127) / 128 * ((T + 127) / 128) < 128) return R_NTILED;
   return R_WIDE;
 }
 

@@ -24,7 +24,8 @@ struct KArgs {
 // error.  `epi` is one of w4dev::EPI_*.
 hipError_t launch_gemv(int bits, int epi, const KArgs& a, hipStream_t stream);      // 1 <= T <= 4
 hipError_t launch_stream16(int bits, int epi, const KArgs& a, hipStream_t stream);  // T <= 16
-hipError_t launch_narrow(int tn, int bits, int epi, const KArgs& a, hipStream_t stream);  // T <= tn
+// narrow: token tiles of tn (32 or 64) columns; T > tn runs ceil(T / tn) token blocks side by side
+hipError_t launch_narrow(int tn, int bits, int epi, const KArgs& a, hipStream_t stream);
 hipError_t launch_wide(int bits, int epi, const KArgs& a, hipStream_t stream);    // any T
 hipError_t launch_splitk(int bits, int epi, const KArgs& a, hipStream_t stream);  // T <= 32
 

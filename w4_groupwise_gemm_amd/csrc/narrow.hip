@@ -244,6 +244,14 @@ template <int BITS, int NP, int NTT, int NC, int DC, int DX, int EPI>
 __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
   using CS = CodeStage<BITS, NP>;
   constexpr int BN = 32 * NTT, XB = BN * 256;
+  // token block blockIdx.y: tokens BN y .. BN y + BN - 1 (more than one only when T > BN)
+  if (blockIdx.y > 0) {
+    const size_t t0 = (size_t)blockIdx.y * BN;
+    a.x += t0 * a.K;
+    a.out += t0 * a.ldo;
+    if (a.res) a.res += t0 * a.ldo;
+    a.T -= (int)t0;
+  }
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const cring = smem;
   char* const xring = smem + DC * CS::kBytes;
@@ -386,7 +394,9 @@ hipError_t run(const KArgs& a, hipStream_t stream) {
   const size_t rings = (size_t)DC * CS::kBytes + (size_t)DX * BN * 256;
   const size_t red = (size_t)NC * NP * NTT * 16 * 64 * 4;
   const size_t lds = rings > red ? rings : red;
-  hipLaunchKernelGGL((narrow_kernel<BITS, NP, NTT, NC, DC, DX, EPI>), dim3(grid),
+  const int ntb = (a.T + BN - 1) / BN;
+  if (ntb > 65535) return hipErrorInvalidConfiguration;  // grid y limit (T above 4 million)
+  hipLaunchKernelGGL((narrow_kernel<BITS, NP, NTT, NC, DC, DX, EPI>), dim3(grid, ntb),
                      dim3(64 * (NC + 2)), lds, stream, a);
   return hipGetLastError();
 }

@@ -219,7 +219,7 @@ __device__ __forceinline__ void consume(const KArgs& a, const char* cring, const
     if (kb + 1 < KB) read(kb + 1, other);
     if (ST::kJ0 < 2 || !(half_last && kb == KB - 1)) math(mine);
   };
-  arrive_wait();  // B(-1): block 0 is in LDS
+  // (barrier B(-1), block 0 in LDS, was passed by the caller)
   read(0, f0);
   int kb = 0;
   for (; kb + 1 < KB; kb += 2) {
@@ -274,8 +274,10 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
   }
 
   // Producers start streaming at once; the consumers vote on the zero-points meanwhile: are all
-  // of this workgroup's zero-points integers (1024 + z exact in fp16)?
-  bool exact = true;
+  // of this workgroup's zero-points integers (1024 + z exact in fp16)?  The votes meet in LDS
+  // at barrier B(-1), which the producers reach as soon as their first block has landed (a
+  // fenced barrier here would hold them until their whole prologue had).
+  __shared__ int votes[NC];
   if (wave == NC) {
 #pragma unroll
     for (int j = 0; j < DC; ++j)
@@ -287,21 +289,38 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
     const int zbase = 2 * pair0 * KB * 64;  // bytes: zero-points of the workgroup's tiles
     const int zbytes = 2 * NP * KB * 64;
     const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f};
-    for (int off = threadIdx.x * 16; off < zbytes; off += 64 * NC * 16) {
-      // past the last tile the range check reads zeros (integers)
-      const u32x4 zz = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.z, zbase + off, 0, 0));
+    constexpr int STEP = 64 * NC * 16;  // bytes per load instruction of all consumers
+    bool exact = true;
+    for (int off0 = threadIdx.x * 16; off0 < zbytes; off0 += 4 * STEP) {
+      // four loads in flight per pass (one pass up to K = 8192 with two pairs); past the last
+      // tile the range check reads zeros (integers)
+      u32x4 zz[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        exact = exact && (__builtin_bit_cast(uint32_t, (as_h2(zz[e]) + c1024) - c1024) == zz[e]);
+      for (int u = 0; u < 4; ++u)
+        zz[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.z, zbase + off0 + u * STEP, 0, 0));
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          exact = exact && (off0 + u * STEP >= zbytes ||
+                            __builtin_bit_cast(uint32_t, (as_h2(zz[u][e]) + c1024) - c1024) == zz[u][e]);
     }
+    const bool all = __ballot(exact) == ~0ull;
+    if (lane == 0) votes[wave] = all ? 1 : 0;
   }
-  const bool fast = __syncthreads_and(exact);
 
   f32x16 acc[NP][NTT];
 #pragma unroll
   for (int p = 0; p < NP; ++p)
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[p][tt] = f32x16{};
+
+  if (wave < NC) {
+    arrive_wait();  // B(-1): block 0 is in LDS, and so are the votes
+  }
+  bool fast = true;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) fast = fast && (wave >= NC || votes[c] != 0);
 
   if (wave == NC) {
     produce<DC, CS::kOps>(KB, [&](int st, int kb) {

@@ -265,12 +265,20 @@ __global__ __launch_bounds__(256, OCC) void wide_kernel(KArgs a, int nrb, int nt
     const int zbase = rb * TILES * a.KB * 64;  // bytes: zero-points of the row block
     const int zbytes = TILES * a.KB * 64;
     const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f};
-    for (int off = threadIdx.x * 16; off < zbytes; off += 256 * 16) {
+    constexpr int STEP = 256 * 16;  // bytes per load instruction of the workgroup
+    for (int off0 = threadIdx.x * 16; off0 < zbytes; off0 += 8 * STEP) {
+      // eight loads in flight per pass (one pass up to K = 6144 with 160-row workgroups);
       // whole offset in the range-checked lane operand: rows past the last tile read zero
-      const u32x4 zz = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.z, zbase + off, 0, 0));
+      u32x4 zz[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        exact = exact && (__builtin_bit_cast(uint32_t, (as_h2(zz[e]) + c1024) - c1024) == zz[e]);
+      for (int u = 0; u < 8; ++u)
+        zz[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.z, zbase + off0 + u * STEP, 0, 0));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          exact = exact && (off0 + u * STEP >= zbytes ||
+                            __builtin_bit_cast(uint32_t, (as_h2(zz[u][e]) + c1024) - c1024) == zz[u][e]);
     }
   }
   if (__syncthreads_and(exact))

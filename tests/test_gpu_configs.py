@@ -21,7 +21,7 @@ NCOLS = 96  # sampled output columns per (configuration, width)
 
 CASES = [("tiny", 1)] + [("decode", t) for t in (1, 2, 4)] + \
         [("batched", t) for t in (8, 16, 32, 64)] + [("swiglu", t) for t in (1, 4, 16, 64)] + \
-        [("prefill", t) for t in (1024, 4096)]
+        [("prefill", t) for t in (128, 384, 1024, 4096)]  # 128, 384: the token-tiled narrow route
 
 
 @functools.lru_cache(maxsize=1)
@@ -47,7 +47,9 @@ def _prepared(name):
 @pytest.mark.parametrize("name,T", CASES, ids=[f"{n}-T{t}" for n, t in CASES])
 def test_config_full_size(name, T):
     wl, pw, canon, bits = _prepared(name)
-    print(f"case config={name} T={T} N={pw.N} K={pw.K} bits={bits} op={wl.op}", flush=True)
+    op = {"swiglu": w4.OP_SWIGLU, "add": w4.OP_ADD}.get(wl.op, w4.OP_LINEAR)
+    route = w4.route_name(w4.route_for(op, bits, T, pw.N, pw.K))
+    print(f"case config={name} T={T} N={pw.N} K={pw.K} bits={bits} op={wl.op} route={route}", flush=True)
     x = wl.x[:T]
     xd = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
     if wl.op == "swiglu":

@@ -230,6 +230,9 @@ def main() -> int:
     g_warm = capture(rotation(max(1, args.warmup)))
     g_steps = capture(rotation(args.steps))
     g_width = {T: capture([(T, c) for c in range(copies)]) for T in widths}
+    # the same number of launches, all on copy 0: the "hot" figure, weights served partly by the
+    # 256 MB Infinity Cache (context only; every headline figure above is cold)
+    g_hot = {T: capture([(T, 0) for _ in range(copies)]) for T in widths}
     g_warm.replay()
     for g in g_width.values():
         g.replay()
@@ -243,25 +246,32 @@ def main() -> int:
     wall = time.perf_counter() - t0
 
     # per-launch duration of each width: HIP events around replays of `copies` back-to-back
-    # launches of that width (one per cold copy), on the launch stream
-    reps = 5
+    # launches of that width (one per cold copy), on the launch stream; 20 replays, mean with a
+    # bootstrap 95% interval
+    reps = 20
+
+    def replay_us(g):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / copies  # us per launch
+
+    boot = np.random.default_rng(12345)
     per_T = {}
     for T in widths:
-        samples = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g_width[T].replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            samples.append(e0.elapsed_time(e1) * 1e3 / copies)  # us per launch
-        d = np.array(samples)
+        d = np.array([replay_us(g_width[T]) for _ in range(reps)])
+        means = boot.choice(d, size=(2000, d.size), replace=True).mean(axis=1)
+        ci = [float(np.percentile(means, 2.5)), float(np.percentile(means, 97.5))]
+        hot = float(np.median([replay_us(g_hot[T]) for _ in range(5)]))
         alg_bytes = wstream_alg + T * K * 2 + T * N * 2 * (2 if op == w4.OP_ADD else 1)
         flops = 2.0 * T * rows * K
         rid = args.route if args.route >= 0 else w4.route_for(op, bits, T, N, K)
         per_T[str(T)] = {
-            "route": w4.route_name(rid), "us_mean": float(d.mean()), "us_min": float(d.min()),
-            "us_max": float(d.max()), "launches_timed": reps * copies,
+            "route": w4.route_name(rid), "us_mean": float(d.mean()), "us_ci95": ci,
+            "us_min": float(d.min()), "us_max": float(d.max()), "launches_timed": reps * copies,
+            "us_hot_mall": hot,
             "weight_GBs": wstream_alg / (d.mean() * 1e3), "alg_GBs": alg_bytes / (d.mean() * 1e3),
             "TFLOPs": flops / (d.mean() * 1e6), "alg_bytes": alg_bytes,
         }
@@ -515,6 +525,35 @@ def cpu_baseline(wl, widths, op, bits, lo, hi, sc, ze, wstream_alg, prefill, row
         threads = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    host = {"cpu_model": cpu_model, "host_cpus": len(os.sched_getaffinity(0)), "blas_threads": threads}
+
+    # the two phases of the oracle timed apart, for one call at the widest T (the first matrix
+    # of the op): unpack + dequantise, then the fp64 product
+    Tw = min(max(widths), 64)
+    xw = wl.x[:Tw].astype(np.float64)
+    m0 = wl.weights[0] if op == 1 else None
+    mlo, mhi, msc, mze = (m0.lo, m0.hi, m0.scales, m0.zeros) if op == 1 else (lo, hi, sc, ze)
+    t_dq = t_mm = 0.0
+    for n0 in range(0, mlo.shape[0], 2048):
+        n1 = min(mlo.shape[0], n0 + 2048)
+        t0 = time.perf_counter()
+        q = oracle.unpack_codes(mlo[n0:n1], None if mhi is None else mhi[n0:n1], K, bits)
+        wdq = oracle.dequantize(q, msc[n0:n1], mze[n0:n1])
+        t1 = time.perf_counter()
+        _ = xw @ wdq.T
+        t2 = time.perf_counter()
+        t_dq += t1 - t0
+        t_mm += t2 - t1
+    host["phases_one_call"] = {"T": Tw, "dequant_s": t_dq, "matmul_s": t_mm}
     if prefill:
         # one token chunk of 64 over the full weight: scaled by FLOPs
         T = 64
@@ -525,7 +564,7 @@ def cpu_baseline(wl, widths, op, bits, lo, hi, sc, ze, wstream_alg, prefill, row
         dt = time.perf_counter() - t0
         return ({"value": 2.0 * T * rows * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
                  "kind": "oracle", "sample": f"T={T} tokens over the full {rows}x{K} weight, "
-                                              f"{dt:.1f} s"}, parity)
+                                              f"{dt:.1f} s", **host}, parity)
     reps, total, t_start = 0, 0.0, time.perf_counter()
     while True:
         for T in widths:
@@ -541,7 +580,7 @@ def cpu_baseline(wl, widths, op, bits, lo, hi, sc, ze, wstream_alg, prefill, row
             break
     return ({"value": reps * len(widths) * wstream_alg / total / 1e9, "unit": "GB/s",
              "cores": threads, "kind": "oracle",
-             "sample": f"{reps} full steps (T in {list(widths)}), {total:.1f} s"}, parity)
+             "sample": f"{reps} full steps (T in {list(widths)}), {total:.1f} s", **host}, parity)
 
 
 if __name__ == "__main__":

@@ -21,7 +21,7 @@ DEV = "cuda:0"
 
 ROUTE_TS = {
     "gemv_exact_t": (1, 2, 3, 4),
-    "mfma_stream_t16": (1, 2, 4, 5, 16),
+    "mfma_stream_t16": (1, 2, 4, 5, 8, 9, 16),
     "mfma_narrow_t32": (3, 17, 32),
     "mfma_narrow_t64": (33, 40, 64),
     "mfma_wide": (1, 65, 129, 300),

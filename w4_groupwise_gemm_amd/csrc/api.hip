@@ -116,10 +116,12 @@ int device_check() {
 // beyond that while the wide kernel's grid is small; the wide kernel above.
 int pick_route(int op, int bits, int T, int N, int K) {
   (void)bits;
-  (void)K;
-  // the SwiGLU pair streams two row tiles per workgroup, which keeps the streaming route ahead
-  // up to its 16-token limit
-  if (T <= 10 || (op == W4_OP_SWIGLU && T <= 16)) return R_N16;
+  // The streaming route holds the activation slice of each wave in LDS up to K = 5120 (16 token
+  // rows), which keeps it ahead up to its 16-token limit there (11264 x 5120, T = 16: 11.5 us
+  // against 16.0 with split K); beyond, its activation fragments ride in the load ring and split
+  // K takes over after T = 10.  The SwiGLU pair streams two row tiles per workgroup, which
+  // keeps the streaming route ahead up to 16 tokens at any K.
+  if (T <= 10 || (T <= 16 && (op == W4_OP_SWIGLU || K <= 5120))) return R_N16;
   if (T <= 18) return R_SPLITK;
   if (T <= 32) return R_N32;
   if (T <= 64) return R_N64;

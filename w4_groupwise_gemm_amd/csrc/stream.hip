@@ -14,10 +14,13 @@
 //  * each wave keeps a ring of D k-blocks of loads in flight ahead of the math (with one row
 //    tile, all of its blocks: the stream never waits for the math); code loads are
 //    non-temporal (each byte is read once per call);
-//  * for T <= 4 the wave's activation slice (T rows of its K range) is loaded first and
-//    parked in a wave-private LDS region, so activation reads never wait behind code loads in
-//    the in-order load counter and no barrier is needed inside the loop; for larger T the
-//    16-token activation fragments ride in the same ring as the codes;
+//  * the wave's activation slice (the token rows of its k-blocks) is loaded first and parked
+//    in a wave-private LDS region, so activation reads never wait behind code loads in the
+//    in-order load counter and no barrier is needed inside the loop: 4 rows through registers
+//    for T <= 4; for K <= 5120, 8 or 16 rows straight from memory (direct-to-LDS loads, no
+//    registers), with 2 or 3 row tiles per workgroup since the slice then allows only one or
+//    two workgroups per compute unit; otherwise the 16-token activation fragments ride in the
+//    same ring as the codes;
 //  * the dequantisation is 13 vector ops per packed word when the zero-points of a block are
 //    integers (checked exactly, wave-uniformly, per block): mask-or the nibbles into the
 //    mantissa of fp16 1024 (one v_and_or_b32 per pair), subtract 1024 + z (or fold 1/16 and
@@ -93,6 +96,14 @@ __device__ __forceinline__ void weights(uint32_t w, uint32_t hiw, uint32_t magic
   }
 }
 
+// Wait until at most n vector-memory operations of this wave are outstanding (vmcnt in bits
+// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int BITS, int RT, int KPW, int XL>
 struct Ring {
   u32x4 cw[KPW][RT];
@@ -100,8 +111,10 @@ struct Ring {
   u32x4 xb[XL ? 1 : KPW][4];
 };
 
+// XL: token rows of the activation slice held in LDS (0: fragments in the ring instead; 4, 8
+// or 16).  xdim: XL = 4, fp16 elements per slice row (padded); XL >= 8, k-blocks of the slice.
 template <int BITS, int MODE, int RT, int NW, int KPW, int D, int XL, int EPI, bool LOOP>
-__global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
+__global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int BLK = block_bytes(BITS);
   const int lane = threadIdx.x & 63;
@@ -114,7 +127,20 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
   const int T = a.T;
   const int tr = min(r, T - 1);
   const uint32_t magic = vgpr_const(0x64006400u);
-  _Float16* xs = reinterpret_cast<_Float16*>(smem) + (size_t)wave * 4 * xstride;
+  // Wave-private activation slice.  4 rows: row t holds the chunk's blocks back to back, rows
+  // xdim elements apart (16 bytes of padding: the rows a fragment read touches hit distinct
+  // banks).  8 / 16 rows: XL x 256 B per k-block, block after block, 16-byte chunk j of row t
+  // stored at chunk j ^ t (no padding: at K = 5120 two 8-row or one 16-row workgroup slice
+  // fill the LDS exactly).
+  constexpr int XBLK = XL * 256;
+  char* const xs = smem + (size_t)wave * (XL >= 8 ? xdim * XBLK : XL * xdim * 2);
+  // 16-byte chunk c (0..15) of token row t of local block i
+  auto xchunk = [&](int i, int t, int c) -> const char* {
+    if constexpr (XL >= 8)
+      return xs + i * XBLK + t * 256 + ((c ^ t) << 4);
+    else
+      return xs + (t * xdim + i * 128 + c * 8) * 2;
+  };
 
   f32x4 acc[RT];
   float accd[RT][4];
@@ -132,11 +158,13 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
   for (int cb = 0; LOOP ? cb < nbw : (cb == 0 && cb < nbw); cb += KPW) {
     const int nb = min(KPW, nbw - cb);
 
-    // activation slice of this chunk (T <= 4 rows, nb k-blocks of 128 columns, parked in LDS
-    // back to back), loaded before any code of the chunk
+    // activation slice of this chunk, loaded before any code of the chunk.  4 rows: T <= 4 rows
+    // of nb k-blocks through registers.  8 / 16 rows: one direct-to-LDS instruction per 4 token
+    // rows of a block (lane L: row 4h + L/16, stored chunk L%16 = source chunk (L%16) ^ row);
+    // rows at or beyond T lie past the end of the range-checked buffer and read as zero.
     constexpr int XCH = (KPW * 16 + 63) / 64;  // 16-byte chunks per lane per token row
-    u32x4 xr[XL ? 4 : 1][XL ? XCH : 1];
-    if constexpr (XL == 1) {
+    u32x4 xr[XL == 4 ? 4 : 1][XL == 4 ? XCH : 1];
+    if constexpr (XL == 4) {
       const int cpt = nb * 16;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -147,6 +175,22 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
             const int kk = min((wave + NW * (cb + (c >> 4))) * 128 + (c & 15) * 8, a.K - 8);
             xr[t][i] = *reinterpret_cast<const u32x4*>(a.x + (size_t)t * a.K + kk);
           }
+        }
+      }
+    } else if constexpr (XL >= 8) {
+      static_assert(!LOOP, "8- and 16-row slices hold one chunk");
+      const auto xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.x), (short)0,
+                                                          (int)((size_t)a.T * a.K * 2), 0x00020000);
+#pragma unroll
+      for (int ib = 0; ib < KPW; ++ib) {
+        // (KPW == nb here: the launcher picks the chunk size equal to the wave's block count)
+        const int kb = wave + NW * ib;
+#pragma unroll
+        for (int h = 0; h < XL / 4; ++h) {
+          const int t = 4 * h + (lane >> 4);
+          const int off = (t * a.K + kb * 128 + (((lane & 15) ^ t) << 3)) * 2;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (__attribute__((address_space(3))) void*)(xs + ib * XBLK + h * 1024),
+                                                   16, off, 0, 0, 0);
         }
       }
     }
@@ -182,7 +226,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
 #pragma unroll
     for (int i = 0; i < D; ++i) issue(i);
 
-    if constexpr (XL == 1) {
+    if constexpr (XL == 4) {
       const int cpt = nb * 16;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -190,13 +234,16 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
 #pragma unroll
           for (int i = 0; i < XCH; ++i) {
             const int c = lane + 64 * i;
-            if (c < cpt) *reinterpret_cast<u32x4*>(xs + t * xstride + c * 8) = xr[t][i];
+            if (c < cpt) *reinterpret_cast<u32x4*>(xs + (t * xdim + c * 8) * 2) = xr[t][i];
           }
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else if constexpr (XL >= 8) {
+      // the slice has landed once at most the ring prologue's loads are outstanding
+      wait_vmcnt<D * RT * (BITS == 5 ? 4 : 3)>();
     }
 
 #pragma unroll
@@ -211,8 +258,8 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
         if constexpr (MODE == MODE_MFMA) {
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
-            if constexpr (XL == 1)
-              Bf[J] = *reinterpret_cast<const f16x8*>(xs + tr * xstride + i * 128 + 64 * (J >> 1) + 16 * g + 8 * (J & 1));
+            if constexpr (XL > 0)
+              Bf[J] = *reinterpret_cast<const f16x8*>(xchunk(i, tr, 8 * (J >> 1) + 2 * g + (J & 1)));
             else
               Bf[J] = __builtin_bit_cast(f16x8, R.xb[i][J]);
           }
@@ -270,11 +317,11 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xstride) {
               if (half_block && J >= 2) return;
               f16x2 wv[4];
               wts(jc, fast, wv);
-              const int koff = i * 128 + 64 * (J >> 1) + 16 * g + 8 * (J & 1);
+              const int c = 8 * (J >> 1) + 2 * g + (J & 1);
 #pragma unroll
               for (int t = 0; t < 4; ++t) {
                 if (t < T) {
-                  const u32x4 xv = *reinterpret_cast<const u32x4*>(xs + t * xstride + koff);
+                  const u32x4 xv = *reinterpret_cast<const u32x4*>(xchunk(i, t, c));
                   float v = accd[rt][t];
 #pragma unroll
                   for (int p = 0; p < 4; ++p) v = __builtin_amdgcn_fdot2(wv[p], as_h2(xv[p]), v, false);
@@ -361,12 +408,16 @@ constexpr int kNW = 8;  // waves per workgroup (K split)
 // Ring depth (k-blocks of loads in flight ahead of the math).  One row tile with the
 // activation slice in LDS: 5, every block of a 5120-column wave in flight at once (decode
 // 12288 x 5120, T = 1: 11.1 us with 3, 10.6 us with 5).  Activation fragments in the ring
-// (T > 4): 3, since each stage then costs 16 more registers.  Two row tiles: 2, where the
-// smaller register footprint buys more resident waves (SwiGLU pair, 34816 packed rows, T = 1:
-// 26.5 us against 30.0 us with 3).  Never deeper than the chunk.
+// (T > 4): 3, since each stage then costs 16 more registers.  Two row tiles with a 4-row
+// slice: 2, where the smaller register footprint buys more resident waves (SwiGLU pair, 34816
+// packed rows, T = 1: 26.5 us against 30.0 us with 3).  Two row tiles with an 8-row slice: the
+// 80 KB slice already limits a compute unit to two workgroups, so all 5 blocks.  Never deeper
+// than the chunk.  Three row tiles with an 8- or 16-row slice: likewise 5.  Six row tiles (the
+// SwiGLU pair with a 16-row slice): 2, within the registers of the one workgroup per compute
+// unit that the slice allows.
 template <int RT, int XL, int KPW>
 constexpr int ring_depth() {
-  constexpr int d = RT >= 2 ? 2 : (XL ? 5 : 3);
+  constexpr int d = XL >= 8 ? (RT >= 6 ? 2 : 5) : RT >= 2 ? 2 : (XL ? 5 : 3);
   return d < KPW ? d : KPW;
 }
 
@@ -375,12 +426,12 @@ hipError_t run_k(const KArgs& a, hipStream_t stream) {
   const int ntiles = a.rows / 16;
   const int nbw = (a.KB + kNW - 1) / kNW;
   const int nbc = nbw < KPW ? nbw : KPW;  // blocks per chunk
-  const int xstride = nbc * 128 + 8;
-  size_t lds = XL ? (size_t)kNW * 4 * xstride * 2 : 0;
+  const int xdim = XL >= 8 ? nbc : nbc * 128 + 8;
+  size_t lds = XL >= 8 ? (size_t)kNW * nbc * XL * 256 : XL == 4 ? (size_t)kNW * 4 * xdim * 2 : 0;
   const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * 64 * 16 : (size_t)kNW * RT * 64 * 4;
   if (red > lds) lds = red;
   hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, ring_depth<RT, XL, KPW>(), XL, EPI, LOOP>),
-                     dim3((ntiles + RT - 1) / RT), dim3(kNW * 64), lds, stream, a, xstride);
+                     dim3((ntiles + RT - 1) / RT), dim3(kNW * 64), lds, stream, a, xdim);
   return hipGetLastError();
 }
 
@@ -394,25 +445,48 @@ hipError_t run(const KArgs& a, hipStream_t stream) {
   if (nbw == 3) return run_k<BITS, MODE, RT, XL, EPI, 3, false>(a, stream);
   if (nbw == 4) return run_k<BITS, MODE, RT, XL, EPI, 4, false>(a, stream);
   if (nbw == 5) return run_k<BITS, MODE, RT, XL, EPI, 5, false>(a, stream);
-  if (nbw <= 8) return run_k<BITS, MODE, RT, XL, EPI, 8, false>(a, stream);
-  if (nbw <= 16) return run_k<BITS, MODE, RT, XL, EPI, 16, false>(a, stream);
-  return run_k<BITS, MODE, RT, XL, EPI, 8, true>(a, stream);
+  if constexpr (XL >= 8) {
+    return hipErrorInvalidValue;  // 8- and 16-row slices are picked for K <= 5120 only
+  } else {
+    if (nbw <= 8) return run_k<BITS, MODE, RT, XL, EPI, 8, false>(a, stream);
+    if (nbw <= 16) return run_k<BITS, MODE, RT, XL, EPI, 16, false>(a, stream);
+    return run_k<BITS, MODE, RT, XL, EPI, 8, true>(a, stream);
+  }
 }
 
 template <int BITS, int MODE, int XL, int EPI>
 hipError_t pick_rt(const KArgs& a, hipStream_t stream) {
   const int ntiles = a.rows / 16;
   if constexpr (EPI == EPI_SWIGLU) {
-    return run<BITS, MODE, 2, XL, EPI>(a, stream);
+    // the gate / up tiles of one pair; three pairs with a 16-row slice (one 160 KB workgroup
+    // per compute unit: 17408-row pair, T = 16: 36.5 us against 37.6 with one pair)
+    return run<BITS, MODE, XL == 16 ? 6 : 2, XL, EPI>(a, stream);
+  } else if constexpr (XL >= 8) {
+    // an 8-row slice (80 KB at K = 5120) leaves room for two workgroups per compute unit, a
+    // 16-row one for one: three row tiles each keep the tiles of a launch resident at once
+    // (batched 11264 x 5120, T = 8: 10.9 us against 11.6 us with two)
+    return run<BITS, MODE, 3, XL, EPI>(a, stream);
   } else {
     if (ntiles >= 4 * 256 * 2) return run<BITS, MODE, 2, XL, EPI>(a, stream);
     return run<BITS, MODE, 1, XL, EPI>(a, stream);
   }
 }
 
+// Activation slice rows.  Up to K = 5120 (five k-blocks per wave): 8 rows for T = 5..8 and for
+// the SwiGLU pair at T <= 4 (its two-tile workgroups run best with the register-free slice and
+// the full ring: 24.6 against 25.3 us at T = 1), 16 rows for T = 9..16 (SwiGLU pair, T = 16:
+// 36.5 against 44.9 us with fragments in the ring).  Otherwise 4 rows for T <= 4 and fragments
+// in the ring above.
 template <int BITS, int MODE, int EPI>
 hipError_t pick_xl(const KArgs& a, hipStream_t stream) {
-  if (a.T <= 4) return pick_rt<BITS, MODE, 1, EPI>(a, stream);
+  const int nbw = (a.KB + kNW - 1) / kNW;
+  if constexpr (MODE == MODE_MFMA) {
+    if (nbw <= 5) {
+      if (a.T <= 8 && (a.T > 4 || EPI == EPI_SWIGLU)) return pick_rt<BITS, MODE, 8, EPI>(a, stream);
+      if (a.T > 8 && a.T <= 16) return pick_rt<BITS, MODE, 16, EPI>(a, stream);
+    }
+  }
+  if (a.T <= 4) return pick_rt<BITS, MODE, 4, EPI>(a, stream);
   if constexpr (MODE == MODE_MFMA) return pick_rt<BITS, MODE, 0, EPI>(a, stream);
   return hipErrorInvalidValue;
 }

@@ -117,12 +117,13 @@ int device_check() {
 int pick_route(int op, int bits, int T, int N, int K) {
   (void)bits;
   // The streaming route holds the activation slice of each wave in LDS up to K = 5120 (16 token
-  // rows), which keeps it ahead up to its 16-token limit there (11264 x 5120, T = 16: 11.5 us
-  // against 16.0 with split K); beyond, its activation fragments ride in the load ring and split
+  // rows), which keeps it ahead up to its 16-token limit there (11264 x 5120, T = 16: 11.4 us
+  // against 15.8 with split K); beyond, its activation fragments ride in the load ring and split
   // K takes over after T = 10.  The SwiGLU pair streams two row tiles per workgroup, which
-  // keeps the streaming route ahead up to 16 tokens at any K.
+  // keeps the streaming route ahead up to 16 tokens at any K.  From T = 17 the narrow kernel
+  // is ahead of split K (15.8 vs 16.1 us at T = 18).
   if (T <= 10 || (T <= 16 && (op == W4_OP_SWIGLU || K <= 5120))) return R_N16;
-  if (T <= 18) return R_SPLITK;
+  if (T <= 16) return R_SPLITK;
   if (T <= 32) return R_N32;
   if (T <= 64) return R_N64;
   // Above 64 tokens the wide kernel's workgroups (about 128 rows x 128 tokens each) leave most

@@ -18,7 +18,10 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw4gemm.so")
 PROBE_LIB = os.path.join(HERE, "libw4probe.so")  # measurement support (read/copy/empty kernels)
 
-SOURCES = ["api.hip", "stream.hip", "narrow.hip", "splitk.hip", "wide.hip", "repack.cpp"]
+# (source, extra defines, object) -- stream.hip is compiled once per code width and epilogue
+STREAM_PARTS = [("stream.hip", [f"-DW4_STREAM_BITS={b}", f"-DW4_STREAM_EPI={e}"], f"stream_b{b}_e{e}.o")
+                for b in (4, 5) for e in (0, 1, 2)]
+SOURCES = STREAM_PARTS + ["api.hip", "narrow.hip", "splitk.hip", "wide.hip", "repack.cpp"]
 PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")
@@ -29,9 +32,10 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + (DEVICE_FLAGS if src.endswith(".hip") else []) + \
+def _compile(item) -> str:
+    src, defines, objname = item if isinstance(item, tuple) else (item, [], os.path.splitext(item)[0] + ".o")
+    obj = os.path.join(BUILD, objname)
+    cmd = [HIPCC] + COMMON + (DEVICE_FLAGS if src.endswith(".hip") else []) + list(defines) + \
         ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -48,7 +52,7 @@ def _link(objs, out):
     shutil.move(tmp, out)
 
 
-def build(verbose: bool = False, jobs: int = 6) -> str:
+def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every source (always, even if a library exists) and link libw4gemm.so and the
     measurement-support libw4probe.so."""
     os.makedirs(BUILD, exist_ok=True)

@@ -22,8 +22,37 @@ struct KArgs {
 
 // Each launcher enqueues exactly one kernel on `stream` and returns hipSuccess or the launch
 // error.  `epi` is one of w4dev::EPI_*.
-hipError_t launch_gemv(int bits, int epi, const KArgs& a, hipStream_t stream);      // 1 <= T <= 4
-hipError_t launch_stream16(int bits, int epi, const KArgs& a, hipStream_t stream);  // T <= 16
+// streaming kernel (stream.hip, one object per code width b and epilogue e)
+#define W4_STREAM_PART(b, e)                                                    \
+  hipError_t launch_gemv_b##b##_e##e(const KArgs& a, hipStream_t stream);     \
+  hipError_t launch_stream16_b##b##_e##e(const KArgs& a, hipStream_t stream);
+W4_STREAM_PART(4, 0) W4_STREAM_PART(4, 1) W4_STREAM_PART(4, 2)
+W4_STREAM_PART(5, 0) W4_STREAM_PART(5, 1) W4_STREAM_PART(5, 2)
+#undef W4_STREAM_PART
+
+inline hipError_t launch_gemv(int bits, int epi, const KArgs& a, hipStream_t stream) {  // 1 <= T <= 4
+  switch (bits * 4 + epi) {
+    case 16: return launch_gemv_b4_e0(a, stream);
+    case 17: return launch_gemv_b4_e1(a, stream);
+    case 18: return launch_gemv_b4_e2(a, stream);
+    case 20: return launch_gemv_b5_e0(a, stream);
+    case 21: return launch_gemv_b5_e1(a, stream);
+    case 22: return launch_gemv_b5_e2(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+inline hipError_t launch_stream16(int bits, int epi, const KArgs& a, hipStream_t stream) {  // T <= 16
+  switch (bits * 4 + epi) {
+    case 16: return launch_stream16_b4_e0(a, stream);
+    case 17: return launch_stream16_b4_e1(a, stream);
+    case 18: return launch_stream16_b4_e2(a, stream);
+    case 20: return launch_stream16_b5_e0(a, stream);
+    case 21: return launch_stream16_b5_e1(a, stream);
+    case 22: return launch_stream16_b5_e2(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 // narrow: token tiles of tn (32 or 64) columns; T > tn runs ceil(T / tn) token blocks side by side
 hipError_t launch_narrow(int tn, int bits, int epi, const KArgs& a, hipStream_t stream);
 hipError_t launch_wide(int bits, int epi, const KArgs& a, hipStream_t stream);    // any T

@@ -113,7 +113,9 @@ struct Ring {
 
 // XL: token rows of the activation slice held in LDS (0: fragments in the ring instead; 4, 8
 // or 16).  xdim: XL = 4, fp16 elements per slice row (padded); XL >= 8, k-blocks of the slice.
-template <int BITS, int MODE, int RT, int NW, int KPW, int D, int XL, int EPI, bool LOOP>
+// HB: K is not a multiple of 128, so the last k-block holds one group only (without it the
+// per-block test for that case, and its branches, compile away).
+template <int BITS, int MODE, int RT, int NW, int KPW, int D, int XL, int EPI, bool LOOP, bool HB>
 __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int BLK = block_bytes(BITS);
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
         R.zp[i][rt] = a.zr[bi * 16 + r];
       }
       if constexpr (XL == 0) {
-        const bool half_block = (kb * 128 + 64 >= a.K);
+        const bool half_block = HB && (kb * 128 + 64 >= a.K);
         const _Float16* xrow = a.x + (size_t)tr * a.K + kb * 128 + 16 * g;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
       if (i + D < KPW && i + D < nb) issue(i + D);
       if (i < nb) {
         const int kb = wave + NW * (cb + i);
-        const bool half_block = (kb * 128 + 64 >= a.K);
+        const bool half_block = HB && (kb * 128 + 64 >= a.K);
         // activation fragments of the block's four 32-k steps, read before the dequantisation
         // so that the LDS latency hides behind it (a half-empty last block skips steps 2, 3)
         f16x8 Bf[4];
@@ -430,8 +432,13 @@ hipError_t run_k(const KArgs& a, hipStream_t stream) {
   size_t lds = XL >= 8 ? (size_t)kNW * nbc * XL * 256 : XL == 4 ? (size_t)kNW * 4 * xdim * 2 : 0;
   const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * 64 * 16 : (size_t)kNW * RT * 64 * 4;
   if (red > lds) lds = red;
-  hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, ring_depth<RT, XL, KPW>(), XL, EPI, LOOP>),
-                     dim3((ntiles + RT - 1) / RT), dim3(kNW * 64), lds, stream, a, xdim);
+  constexpr int D = ring_depth<RT, XL, KPW>();
+  if (a.K % 128)
+    hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, D, XL, EPI, LOOP, true>),
+                       dim3((ntiles + RT - 1) / RT), dim3(kNW * 64), lds, stream, a, xdim);
+  else
+    hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, D, XL, EPI, LOOP, false>),
+                       dim3((ntiles + RT - 1) / RT), dim3(kNW * 64), lds, stream, a, xdim);
   return hipGetLastError();
 }
 
@@ -491,21 +498,23 @@ hipError_t pick_xl(const KArgs& a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-template <int BITS, int MODE>
-hipError_t pick_epi(int epi, const KArgs& a, hipStream_t stream) {
-  if (epi == EPI_SWIGLU) return pick_xl<BITS, MODE, EPI_SWIGLU>(a, stream);
-  if (epi == EPI_ADD) return pick_xl<BITS, MODE, EPI_ADD>(a, stream);
-  return pick_xl<BITS, MODE, EPI_STORE>(a, stream);
-}
-
 }  // namespace
 
-hipError_t launch_gemv(int bits, int epi, const KArgs& a, hipStream_t stream) {
-  return bits == 5 ? pick_epi<5, MODE_DOT2>(epi, a, stream) : pick_epi<4, MODE_DOT2>(epi, a, stream);
+// This file is compiled once per code width and epilogue (W4_STREAM_BITS, W4_STREAM_EPI), so
+// that the build compiles the six sets of kernel instances in parallel; each object defines the
+// two launchers of its part, and kernels.h dispatches between them.
+#if !defined(W4_STREAM_BITS) || !defined(W4_STREAM_EPI)
+#error "compile with -DW4_STREAM_BITS=4|5 -DW4_STREAM_EPI=0|1|2"
+#endif
+#define W4_PART_NAME2(f, b, e) f##_b##b##_e##e
+#define W4_PART_NAME(f, b, e) W4_PART_NAME2(f, b, e)
+
+hipError_t W4_PART_NAME(launch_gemv, W4_STREAM_BITS, W4_STREAM_EPI)(const KArgs& a, hipStream_t stream) {
+  return pick_xl<W4_STREAM_BITS, MODE_DOT2, W4_STREAM_EPI>(a, stream);
 }
 
-hipError_t launch_stream16(int bits, int epi, const KArgs& a, hipStream_t stream) {
-  return bits == 5 ? pick_epi<5, MODE_MFMA>(epi, a, stream) : pick_epi<4, MODE_MFMA>(epi, a, stream);
+hipError_t W4_PART_NAME(launch_stream16, W4_STREAM_BITS, W4_STREAM_EPI)(const KArgs& a, hipStream_t stream) {
+  return pick_xl<W4_STREAM_BITS, MODE_MFMA, W4_STREAM_EPI>(a, stream);
 }
 
 }  // namespace w4

@@ -20,10 +20,11 @@ DEV = "cuda:0"
 NCOLS = 96  # sampled output columns per (configuration, width)
 
 CASES = [("tiny", 1)] + [("decode", t) for t in (1, 2, 4)] + \
-        [("batched", t) for t in (5, 8, 16, 32, 64)] + [("swiglu", t) for t in (1, 4, 8, 16, 64)] + \
-        [("prefill", t) for t in (128, 384, 1024, 4096)]
-# batched 5, swiglu 8: the 8-row activation slice of the stream kernel at full K; prefill 128,
-# 384: the token-tiled narrow route
+        [("batched", t) for t in (5, 8, 16, 20, 32, 64)] + [("swiglu", t) for t in (1, 4, 8, 16, 24, 64)] + \
+        [("prefill", t) for t in (32, 128, 384, 1024, 4096)]
+# batched 5, swiglu 8: the 8-row activation slice of the stream kernel at full K; batched 20,
+# swiglu 24: its 32-row activation ring at full K; prefill 32: the 32-token route at K > 5120
+# (narrow kernel); prefill 128, 384: the token-tiled narrow route
 
 
 @functools.lru_cache(maxsize=1)

@@ -19,7 +19,7 @@
 
 namespace {
 
-enum RouteKind { KIND_GEMV = 0, KIND_STREAM = 1, KIND_NARROW = 2, KIND_WIDE = 3, KIND_SPLITK = 4 };
+enum RouteKind { KIND_GEMV = 0, KIND_STREAM = 1, KIND_NARROW = 2, KIND_WIDE = 3, KIND_SPLITK = 4, KIND_STREAM32 = 5 };
 
 struct Route {
   const char* name;
@@ -36,9 +36,10 @@ const Route kRoutes[] = {
     {"mfma_wide", 1, INT_MAX, KIND_WIDE, 0},
     {"mfma_splitk_t32", 1, 32, KIND_SPLITK, 32},
     {"mfma_narrow_tiled", 1, INT_MAX, KIND_NARROW, 64},
+    {"mfma_stream_t32", 1, 32, KIND_STREAM32, 32},
 };
 constexpr int kNumRoutes = sizeof(kRoutes) / sizeof(kRoutes[0]);
-enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5, R_NTILED = 6 };
+enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5, R_NTILED = 6, R_S32 = 7 };
 
 constexpr int kMaxDim = 1 << 24;
 
@@ -120,9 +121,12 @@ int pick_route(int op, int bits, int T, int N, int K) {
   // rows), which keeps it ahead up to its 16-token limit there (11264 x 5120, T = 16: 11.4 us
   // against 15.8 with split K); beyond, its activation fragments ride in the load ring and split
   // K takes over after T = 10.  The SwiGLU pair streams two row tiles per workgroup, which
-  // keeps the streaming route ahead up to 16 tokens at any K.  From T = 17 the narrow kernel
-  // is ahead of split K (15.8 vs 16.1 us at T = 18).
+  // keeps the streaming route ahead up to 16 tokens at any K.  For 17-32 tokens and K <= 5120
+  // the streaming kernel's 32-row activation ring is ahead of the narrow kernel (11264 x 5120,
+  // T = 32: 12.5 vs 16.1 us; SwiGLU pair T = 24: 40.6 vs 46.0); beyond that K the narrow kernel
+  // is ahead of split K from T = 17 (15.8 vs 16.1 us at T = 18).
   if (T <= 10 || (T <= 16 && (op == W4_OP_SWIGLU || K <= 5120))) return R_N16;
+  if (T <= 32 && K <= 5120) return R_S32;
   if (T <= 16) return R_SPLITK;
   if (T <= 32) return R_N32;
   if (T <= 64) return R_N64;
@@ -162,6 +166,11 @@ int launch_route(int route, int op, const void* x, const void* w, const void* s,
     case KIND_NARROW: e = w4::launch_narrow(R.tn, bits, epi, a, st); break;
     case KIND_WIDE: e = w4::launch_wide(bits, epi, a, st); break;
     case KIND_SPLITK: e = w4::launch_splitk(bits, epi, a, st); break;
+    case KIND_STREAM32:
+      // the 32-row activation ring of the streaming kernel covers K <= 5120 (five k-blocks per
+      // wave); longer rows run this route's schedule on the narrow kernel's 32-token tile
+      e = K <= 5120 ? w4::launch_stream32(bits, epi, a, st) : w4::launch_narrow(32, bits, epi, a, st);
+      break;
     default: return W4_ERR_DOMAIN;
   }
   return e == hipSuccess ? W4_OK : W4_ERR_LAUNCH;

@@ -104,6 +104,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// The same for an n that is a constant once the caller's loop is unrolled.
+template <int N = 0>
+__device__ __forceinline__ void wait_vmcnt_folded(int n) {
+  if constexpr (N < 63) {
+    if (n == N) {
+      wait_vmcnt<N>();
+      return;
+    }
+    wait_vmcnt_folded<N + 1>(n);
+  } else {
+    wait_vmcnt<63>();
+  }
+}
+
 template <int BITS, int RT, int KPW, int XL>
 struct Ring {
   u32x4 cw[KPW][RT];
@@ -112,7 +126,9 @@ struct Ring {
 };
 
 // XL: token rows of the activation slice held in LDS (0: fragments in the ring instead; 4, 8
-// or 16).  xdim: XL = 4, fp16 elements per slice row (padded); XL >= 8, k-blocks of the slice.
+// or 16; 32: a two-block ring of 32-row activation tiles, refilled as the blocks are consumed,
+// and two 16-token matrix-core steps per weight fragment).  xdim: XL = 4, fp16 elements per
+// slice row (padded); XL = 8 / 16, k-blocks of the slice.
 // HB: K is not a multiple of 128, so the last k-block holds one group only (without it the
 // per-block test for that case, and its branches, compile away).
 template <int BITS, int MODE, int RT, int NW, int KPW, int D, int XL, int EPI, bool LOOP, bool HB>
@@ -134,21 +150,30 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
   // banks).  8 / 16 rows: XL x 256 B per k-block, block after block, 16-byte chunk j of row t
   // stored at chunk j ^ t (no padding: at K = 5120 two 8-row or one 16-row workgroup slice
   // fill the LDS exactly).
+  // 32 rows: two slots of 32 rows x 256 B, block i in slot i % 2, chunk j of row t at
+  // j ^ (t % 16).
+  constexpr int TH = XL == 32 ? 2 : 1;  // 16-token halves per weight fragment
   constexpr int XBLK = XL * 256;
-  char* const xs = smem + (size_t)wave * (XL >= 8 ? xdim * XBLK : XL * xdim * 2);
+  char* const xs = smem + (size_t)wave * (XL == 32 ? 2 * XBLK : XL >= 8 ? xdim * XBLK : XL * xdim * 2);
   // 16-byte chunk c (0..15) of token row t of local block i
   auto xchunk = [&](int i, int t, int c) -> const char* {
-    if constexpr (XL >= 8)
+    if constexpr (XL == 32)
+      return xs + (i & 1) * XBLK + t * 256 + ((c ^ (t & 15)) << 4);
+    else if constexpr (XL >= 8)
       return xs + i * XBLK + t * 256 + ((c ^ t) << 4);
     else
       return xs + (t * xdim + i * 128 + c * 8) * 2;
   };
+  const auto xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.x), (short)0,
+                                                      (int)((size_t)a.T * a.K * 2), 0x00020000);
+  const int tr2 = min(16 + r, T - 1);  // token row of the second 16-token half
 
-  f32x4 acc[RT];
+  f32x4 acc[RT], acc2[TH == 2 ? RT : 1];
   float accd[RT][4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (TH == 2) acc2[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) accd[rt][t] = 0.f;
   }
@@ -179,10 +204,8 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
           }
         }
       }
-    } else if constexpr (XL >= 8) {
+    } else if constexpr (XL == 8 || XL == 16) {
       static_assert(!LOOP, "8- and 16-row slices hold one chunk");
-      const auto xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.x), (short)0,
-                                                          (int)((size_t)a.T * a.K * 2), 0x00020000);
 #pragma unroll
       for (int ib = 0; ib < KPW; ++ib) {
         // (KPW == nb here: the launcher picks the chunk size equal to the wave's block count)
@@ -195,6 +218,24 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
                                                    16, off, 0, 0, 0);
         }
       }
+    }
+
+    // 32 rows: the tiles of local blocks i into ring slot i % 2 (8 direct-to-LDS instructions
+    // of 4 token rows each, laid out as above).
+    auto xload = [&](int i) {
+      const int kb = wave + NW * (cb + min(i, nb - 1));
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const int t = 4 * h + (lane >> 4);
+        const int off = (t * a.K + kb * 128 + (((lane & 15) ^ (t & 15)) << 3)) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (__attribute__((address_space(3))) void*)(xs + (i & 1) * XBLK + h * 1024),
+                                                 16, off, 0, 0, 0);
+      }
+    };
+    if constexpr (XL == 32) {
+      static_assert(!LOOP, "the 32-row ring holds one chunk");
+      xload(0);
+      xload(1);
     }
 
     // Loads of local block i.  The first D blocks are issued unconditionally (a wave with
@@ -243,7 +284,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    } else if constexpr (XL >= 8) {
+    } else if constexpr (XL == 8 || XL == 16) {
       // the slice has landed once at most the ring prologue's loads are outstanding
       wait_vmcnt<D * RT * (BITS == 5 ? 4 : 3)>();
     }
@@ -256,7 +297,14 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
         const bool half_block = HB && (kb * 128 + 64 >= a.K);
         // activation fragments of the block's four 32-k steps, read before the dequantisation
         // so that the LDS latency hides behind it (a half-empty last block skips steps 2, 3)
-        f16x8 Bf[4];
+        f16x8 Bf[4], Bf2[TH == 2 ? 4 : 1];
+        if constexpr (XL == 32) {
+          // the ring tile of block i has landed once at most the loads issued after it are
+          // outstanding: the other blocks' codes (blocks 0, 1) and the next tile's refill
+          constexpr int CPB = RT * (BITS == 5 ? 4 : 3);
+          wait_vmcnt_folded(i == 0 ? (KPW - 1) * CPB
+                                   : i == 1 ? (KPW - 2) * CPB + (2 < KPW ? 8 : 0) : (i + 1 < KPW ? 8 : 0));
+        }
         if constexpr (MODE == MODE_MFMA) {
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
@@ -264,6 +312,8 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
               Bf[J] = *reinterpret_cast<const f16x8*>(xchunk(i, tr, 8 * (J >> 1) + 2 * g + (J & 1)));
             else
               Bf[J] = __builtin_bit_cast(f16x8, R.xb[i][J]);
+            if constexpr (TH == 2)
+              Bf2[J] = *reinterpret_cast<const f16x8*>(xchunk(i, tr2, 8 * (J >> 1) + 2 * g + (J & 1)));
           }
         }
 #pragma unroll
@@ -308,10 +358,14 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
             else
               all_a(false);
             acc[rt] = mfma16(A[0], Bf[0], acc[rt]);
+            if constexpr (TH == 2) acc2[rt] = mfma16(A[0], Bf2[0], acc2[rt]);
             acc[rt] = mfma16(A[1], Bf[1], acc[rt]);
+            if constexpr (TH == 2) acc2[rt] = mfma16(A[1], Bf2[1], acc2[rt]);
             if (!half_block) {
               acc[rt] = mfma16(A[2], Bf[2], acc[rt]);
+              if constexpr (TH == 2) acc2[rt] = mfma16(A[2], Bf2[2], acc2[rt]);
               acc[rt] = mfma16(A[3], Bf[3], acc[rt]);
+              if constexpr (TH == 2) acc2[rt] = mfma16(A[3], Bf2[3], acc2[rt]);
             }
           } else {
             auto dot_j = [&](auto jc) {
@@ -338,36 +392,47 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
           }
         }
       }
+      if constexpr (XL == 32) {
+        if (i + 2 < KPW) {
+          // this wave's reads of slot i % 2 are complete: refill it with block i + 2's tile
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0 (vmcnt, expcnt: no wait)
+          xload(i + 2);
+        }
+      }
     }
   }
 
   // ---- fixed-order combination of the NW partial sums, then the epilogue
   __syncthreads();
   if constexpr (MODE == MODE_MFMA) {
-    f32x4* red = reinterpret_cast<f32x4*>(smem);  // [NW][RT][64]
+    // red[w][h][rt][lane]: wave w's partial sums of token half h, row tile rt
+    f32x4* red = reinterpret_cast<f32x4*>(smem);
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) red[(wave * RT + rt) * 64 + lane] = acc[rt];
+    for (int rt = 0; rt < RT; ++rt) {
+      red[((wave * TH + 0) * RT + rt) * 64 + lane] = acc[rt];
+      if constexpr (TH == 2) red[((wave * TH + 1) * RT + rt) * 64 + lane] = acc2[rt];
+    }
     __syncthreads();
-    constexpr int ITEMS = (EPI == EPI_SWIGLU ? RT / 2 : RT) * 64;
+    auto sum = [&](int h, int rt, int l) {
+      f32x4 v = red[(h * RT + rt) * 64 + l];
+      for (int w = 1; w < NW; ++w) v = v + red[((w * TH + h) * RT + rt) * 64 + l];
+      return v;
+    };
+    constexpr int ITEMS = TH * (EPI == EPI_SWIGLU ? RT / 2 : RT) * 64;
     for (int it = threadIdx.x; it < ITEMS; it += NW * 64) {
-      const int l = it & 63, p = it >> 6;
-      const int t = l & 15;
+      const int l = it & 63, hp = it >> 6;
+      const int h = hp % TH, p = hp / TH;
+      const int t = 16 * h + (l & 15);
       if (t >= T) continue;
       if constexpr (EPI == EPI_SWIGLU) {
         const int gtile = tile0 + 2 * p;
         if (gtile >= ntiles) continue;
-        f32x4 gv = red[(2 * p) * 64 + l], uv = red[(2 * p + 1) * 64 + l];
-        for (int w = 1; w < NW; ++w) {
-          gv = gv + red[(w * RT + 2 * p) * 64 + l];
-          uv = uv + red[(w * RT + 2 * p + 1) * 64 + l];
-        }
-        store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + (gtile >> 1) * 16 + 4 * (l >> 4), gv, uv);
+        store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + (gtile >> 1) * 16 + 4 * (l >> 4), sum(h, 2 * p, l),
+                        sum(h, 2 * p + 1, l));
       } else {
         const int tile = tile0 + p;
         if (tile >= ntiles) continue;
-        f32x4 v = red[p * 64 + l];
-        for (int w = 1; w < NW; ++w) v = v + red[(w * RT + p) * 64 + l];
-        store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + tile * 16 + 4 * (l >> 4), v, f32x4{});
+        store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + tile * 16 + 4 * (l >> 4), sum(h, p, l), f32x4{});
       }
     }
   } else {
@@ -419,7 +484,7 @@ constexpr int kNW = 8;  // waves per workgroup (K split)
 // unit that the slice allows.
 template <int RT, int XL, int KPW>
 constexpr int ring_depth() {
-  constexpr int d = XL >= 8 ? (RT >= 6 ? 2 : 5) : RT >= 2 ? 2 : (XL ? 5 : 3);
+  constexpr int d = XL == 32 ? 5 : XL >= 8 ? (RT >= 6 ? 2 : 5) : RT >= 2 ? 2 : (XL ? 5 : 3);
   return d < KPW ? d : KPW;
 }
 
@@ -429,8 +494,9 @@ hipError_t run_k(const KArgs& a, hipStream_t stream) {
   const int nbw = (a.KB + kNW - 1) / kNW;
   const int nbc = nbw < KPW ? nbw : KPW;  // blocks per chunk
   const int xdim = XL >= 8 ? nbc : nbc * 128 + 8;
-  size_t lds = XL >= 8 ? (size_t)kNW * nbc * XL * 256 : XL == 4 ? (size_t)kNW * 4 * xdim * 2 : 0;
-  const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * 64 * 16 : (size_t)kNW * RT * 64 * 4;
+  size_t lds = XL == 32 ? (size_t)kNW * 2 * 32 * 256
+             : XL >= 8 ? (size_t)kNW * nbc * XL * 256 : XL == 4 ? (size_t)kNW * 4 * xdim * 2 : 0;
+  const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * (XL == 32 ? 2 : 1) * 64 * 16 : (size_t)kNW * RT * 64 * 4;
   if (red > lds) lds = red;
   constexpr int D = ring_depth<RT, XL, KPW>();
   if (a.K % 128)
@@ -515,6 +581,12 @@ hipError_t W4_PART_NAME(launch_gemv, W4_STREAM_BITS, W4_STREAM_EPI)(const KArgs&
 
 hipError_t W4_PART_NAME(launch_stream16, W4_STREAM_BITS, W4_STREAM_EPI)(const KArgs& a, hipStream_t stream) {
   return pick_xl<W4_STREAM_BITS, MODE_MFMA, W4_STREAM_EPI>(a, stream);
+}
+
+// 32-token mode (two-block ring of 32-row activation tiles): K <= 5120 only
+hipError_t W4_PART_NAME(launch_stream32, W4_STREAM_BITS, W4_STREAM_EPI)(const KArgs& a, hipStream_t stream) {
+  if ((a.KB + kNW - 1) / kNW > 5) return hipErrorInvalidValue;
+  return pick_rt<W4_STREAM_BITS, MODE_MFMA, 32, W4_STREAM_EPI>(a, stream);
 }
 
 }  // namespace w4

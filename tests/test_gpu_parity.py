@@ -28,6 +28,7 @@ ROUTE_TS = {
     "mfma_splitk_t32": (1, 7, 17, 32),
     "mfma_narrow_tiled": (1, 33, 65, 129, 200),
     "mfma_stream_t32": (1, 5, 16, 17, 24, 32),
+    "mfma_stream_t64": (1, 17, 33, 40, 64),
 }
 
 

@@ -19,7 +19,7 @@
 
 namespace {
 
-enum RouteKind { KIND_GEMV = 0, KIND_STREAM = 1, KIND_NARROW = 2, KIND_WIDE = 3, KIND_SPLITK = 4, KIND_STREAM32 = 5 };
+enum RouteKind { KIND_GEMV = 0, KIND_STREAM = 1, KIND_NARROW = 2, KIND_WIDE = 3, KIND_SPLITK = 4, KIND_STREAM32 = 5, KIND_STREAM64 = 6 };
 
 struct Route {
   const char* name;
@@ -37,9 +37,10 @@ const Route kRoutes[] = {
     {"mfma_splitk_t32", 1, 32, KIND_SPLITK, 32},
     {"mfma_narrow_tiled", 1, INT_MAX, KIND_NARROW, 64},
     {"mfma_stream_t32", 1, 32, KIND_STREAM32, 32},
+    {"mfma_stream_t64", 1, 64, KIND_STREAM64, 64},
 };
 constexpr int kNumRoutes = sizeof(kRoutes) / sizeof(kRoutes[0]);
-enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5, R_NTILED = 6, R_S32 = 7 };
+enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5, R_NTILED = 6, R_S32 = 7, R_S64 = 8 };
 
 constexpr int kMaxDim = 1 << 24;
 
@@ -129,6 +130,11 @@ int pick_route(int op, int bits, int T, int N, int K) {
   if (T <= 32 && K <= 5120) return R_S32;
   if (T <= 16) return R_SPLITK;
   if (T <= 32) return R_N32;
+  // 33-64 tokens: the streaming kernel's one-slot 64-row ring is a little ahead of the narrow
+  // kernel for single matrices (11264 x 5120, T = 64: 17.9 vs 19.9 us), not for the SwiGLU
+  // pair, whose two-tile workgroups take 4 rounds of the one workgroup per compute unit that
+  // the ring allows (61.5 vs 57.5 us)
+  if (T <= 64 && K <= 5120 && op != W4_OP_SWIGLU) return R_S64;
   if (T <= 64) return R_N64;
   // Above 64 tokens the wide kernel's workgroups (about 128 rows x 128 tokens each) leave most
   // compute units idle until there are about 128 of them; below that the narrow kernel run as
@@ -170,6 +176,9 @@ int launch_route(int route, int op, const void* x, const void* w, const void* s,
       // the 32-row activation ring of the streaming kernel covers K <= 5120 (five k-blocks per
       // wave); longer rows run this route's schedule on the narrow kernel's 32-token tile
       e = K <= 5120 ? w4::launch_stream32(bits, epi, a, st) : w4::launch_narrow(32, bits, epi, a, st);
+      break;
+    case KIND_STREAM64:  // likewise with 64-row tiles
+      e = K <= 5120 ? w4::launch_stream64(bits, epi, a, st) : w4::launch_narrow(64, bits, epi, a, st);
       break;
     default: return W4_ERR_DOMAIN;
   }

@@ -26,7 +26,8 @@ struct KArgs {
 #define W4_STREAM_PART(b, e)                                                    \
   hipError_t launch_gemv_b##b##_e##e(const KArgs& a, hipStream_t stream);     \
   hipError_t launch_stream16_b##b##_e##e(const KArgs& a, hipStream_t stream); \
-  hipError_t launch_stream32_b##b##_e##e(const KArgs& a, hipStream_t stream);
+  hipError_t launch_stream32_b##b##_e##e(const KArgs& a, hipStream_t stream); \
+  hipError_t launch_stream64_b##b##_e##e(const KArgs& a, hipStream_t stream);
 W4_STREAM_PART(4, 0) W4_STREAM_PART(4, 1) W4_STREAM_PART(4, 2)
 W4_STREAM_PART(5, 0) W4_STREAM_PART(5, 1) W4_STREAM_PART(5, 2)
 #undef W4_STREAM_PART
@@ -52,6 +53,19 @@ inline hipError_t launch_stream32(int bits, int epi, const KArgs& a, hipStream_t
     case 20: return launch_stream32_b5_e0(a, stream);
     case 21: return launch_stream32_b5_e1(a, stream);
     case 22: return launch_stream32_b5_e2(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// T <= 64, K <= 5120 (one-slot ring of 64-row activation tiles)
+inline hipError_t launch_stream64(int bits, int epi, const KArgs& a, hipStream_t stream) {
+  switch (bits * 4 + epi) {
+    case 16: return launch_stream64_b4_e0(a, stream);
+    case 17: return launch_stream64_b4_e1(a, stream);
+    case 18: return launch_stream64_b4_e2(a, stream);
+    case 20: return launch_stream64_b5_e0(a, stream);
+    case 21: return launch_stream64_b5_e1(a, stream);
+    case 22: return launch_stream64_b5_e2(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

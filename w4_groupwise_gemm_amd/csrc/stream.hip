@@ -127,7 +127,8 @@ struct Ring {
 
 // XL: token rows of the activation slice held in LDS (0: fragments in the ring instead; 4, 8
 // or 16; 32: a two-block ring of 32-row activation tiles, refilled as the blocks are consumed,
-// and two 16-token matrix-core steps per weight fragment).  xdim: XL = 4, fp16 elements per
+// and two 16-token matrix-core steps per weight fragment; 64: one 64-row tile slot, refilled
+// with the next block's tile as soon as the current one has been read, and four steps).  xdim: XL = 4, fp16 elements per
 // slice row (padded); XL = 8 / 16, k-blocks of the slice.
 // HB: K is not a multiple of 128, so the last k-block holds one group only (without it the
 // per-block test for that case, and its branches, compile away).
@@ -150,15 +151,17 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
   // banks).  8 / 16 rows: XL x 256 B per k-block, block after block, 16-byte chunk j of row t
   // stored at chunk j ^ t (no padding: at K = 5120 two 8-row or one 16-row workgroup slice
   // fill the LDS exactly).
-  // 32 rows: two slots of 32 rows x 256 B, block i in slot i % 2, chunk j of row t at
-  // j ^ (t % 16).
-  constexpr int TH = XL == 32 ? 2 : 1;  // 16-token halves per weight fragment
+  // 32 / 64 rows: two / one slots of XL rows x 256 B (block i in slot i % 2 / slot 0), chunk j
+  // of row t at j ^ (t % 16).
+  constexpr bool RING = XL >= 32;
+  constexpr int TH = RING ? XL / 16 : 1;  // 16-token groups per weight fragment
+  constexpr int NSLOT = XL == 32 ? 2 : 1;
   constexpr int XBLK = XL * 256;
-  char* const xs = smem + (size_t)wave * (XL == 32 ? 2 * XBLK : XL >= 8 ? xdim * XBLK : XL * xdim * 2);
+  char* const xs = smem + (size_t)wave * (RING ? NSLOT * XBLK : XL >= 8 ? xdim * XBLK : XL * xdim * 2);
   // 16-byte chunk c (0..15) of token row t of local block i
   auto xchunk = [&](int i, int t, int c) -> const char* {
-    if constexpr (XL == 32)
-      return xs + (i & 1) * XBLK + t * 256 + ((c ^ (t & 15)) << 4);
+    if constexpr (RING)
+      return xs + (i % NSLOT) * XBLK + t * 256 + ((c ^ (t & 15)) << 4);
     else if constexpr (XL >= 8)
       return xs + i * XBLK + t * 256 + ((c ^ t) << 4);
     else
@@ -166,14 +169,14 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
   };
   const auto xres = __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(a.x), (short)0,
                                                       (int)((size_t)a.T * a.K * 2), 0x00020000);
-  const int tr2 = min(16 + r, T - 1);  // token row of the second 16-token half
-
-  f32x4 acc[RT], acc2[TH == 2 ? RT : 1];
+  // acc: tokens 0..15; accx[q - 1]: tokens 16 q .. 16 q + 15
+  f32x4 acc[RT], accx[TH > 1 ? TH - 1 : 1][RT];
   float accd[RT][4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (TH == 2) acc2[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q + 1 < TH; ++q) accx[q][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) accd[rt][t] = 0.f;
   }
@@ -218,24 +221,28 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
                                                    16, off, 0, 0, 0);
         }
       }
+      // the waits below count loads issued after the slice: keep every slice load ahead of the
+      // code loads (the scheduler may otherwise interleave them)
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // 32 rows: the tiles of local blocks i into ring slot i % 2 (8 direct-to-LDS instructions
-    // of 4 token rows each, laid out as above).
+    // 32 / 64 rows: the tile of local block i into its ring slot (XL / 4 direct-to-LDS
+    // instructions of 4 token rows each, laid out as above).
     auto xload = [&](int i) {
       const int kb = wave + NW * (cb + min(i, nb - 1));
 #pragma unroll
-      for (int h = 0; h < 8; ++h) {
+      for (int h = 0; h < XL / 4; ++h) {
         const int t = 4 * h + (lane >> 4);
         const int off = (t * a.K + kb * 128 + (((lane & 15) ^ (t & 15)) << 3)) * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (__attribute__((address_space(3))) void*)(xs + (i & 1) * XBLK + h * 1024),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (__attribute__((address_space(3))) void*)(xs + (i % NSLOT) * XBLK + h * 1024),
                                                  16, off, 0, 0, 0);
       }
     };
-    if constexpr (XL == 32) {
-      static_assert(!LOOP, "the 32-row ring holds one chunk");
+    if constexpr (RING) {
+      static_assert(!LOOP, "the activation ring holds one chunk");
       xload(0);
-      xload(1);
+      if constexpr (NSLOT == 2) xload(1);
+      __builtin_amdgcn_sched_barrier(0);  // (as for the slice: the waits count loads after these)
     }
 
     // Loads of local block i.  The first D blocks are issued unconditionally (a wave with
@@ -297,13 +304,18 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
         const bool half_block = HB && (kb * 128 + 64 >= a.K);
         // activation fragments of the block's four 32-k steps, read before the dequantisation
         // so that the LDS latency hides behind it (a half-empty last block skips steps 2, 3)
-        f16x8 Bf[4], Bf2[TH == 2 ? 4 : 1];
+        f16x8 Bf[4], Bx[TH > 1 ? TH - 1 : 1][4];
         if constexpr (XL == 32) {
           // the ring tile of block i has landed once at most the loads issued after it are
           // outstanding: the other blocks' codes (blocks 0, 1) and the next tile's refill
           constexpr int CPB = RT * (BITS == 5 ? 4 : 3);
           wait_vmcnt_folded(i == 0 ? (KPW - 1) * CPB
                                    : i == 1 ? (KPW - 2) * CPB + (2 < KPW ? 8 : 0) : (i + 1 < KPW ? 8 : 0));
+        } else if constexpr (XL == 64) {
+          // block 0's tile was issued before every code load; each later tile is the last load
+          // issued
+          constexpr int CPB = RT * (BITS == 5 ? 4 : 3);
+          wait_vmcnt_folded(i == 0 ? KPW * CPB : 0);
         }
         if constexpr (MODE == MODE_MFMA) {
 #pragma unroll
@@ -312,8 +324,18 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
               Bf[J] = *reinterpret_cast<const f16x8*>(xchunk(i, tr, 8 * (J >> 1) + 2 * g + (J & 1)));
             else
               Bf[J] = __builtin_bit_cast(f16x8, R.xb[i][J]);
-            if constexpr (TH == 2)
-              Bf2[J] = *reinterpret_cast<const f16x8*>(xchunk(i, tr2, 8 * (J >> 1) + 2 * g + (J & 1)));
+#pragma unroll
+            for (int q = 0; q + 1 < TH; ++q)
+              Bx[q][J] = *reinterpret_cast<const f16x8*>(xchunk(i, min(16 * (q + 1) + r, T - 1), 8 * (J >> 1) + 2 * g + (J & 1)));
+          }
+        }
+        if constexpr (XL == 64) {
+          if (i + 1 < KPW) {
+            // the tile has been read: refill the slot with the next block's tile under this
+            // block's math
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0 (vmcnt, expcnt: no wait)
+            xload(i + 1);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
 #pragma unroll
@@ -357,15 +379,16 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
               all_a(true);
             else
               all_a(false);
-            acc[rt] = mfma16(A[0], Bf[0], acc[rt]);
-            if constexpr (TH == 2) acc2[rt] = mfma16(A[0], Bf2[0], acc2[rt]);
-            acc[rt] = mfma16(A[1], Bf[1], acc[rt]);
-            if constexpr (TH == 2) acc2[rt] = mfma16(A[1], Bf2[1], acc2[rt]);
+            auto steps = [&](int J) {
+              acc[rt] = mfma16(A[J], Bf[J], acc[rt]);
+#pragma unroll
+              for (int q = 0; q + 1 < TH; ++q) accx[q][rt] = mfma16(A[J], Bx[q][J], accx[q][rt]);
+            };
+            steps(0);
+            steps(1);
             if (!half_block) {
-              acc[rt] = mfma16(A[2], Bf[2], acc[rt]);
-              if constexpr (TH == 2) acc2[rt] = mfma16(A[2], Bf2[2], acc2[rt]);
-              acc[rt] = mfma16(A[3], Bf[3], acc[rt]);
-              if constexpr (TH == 2) acc2[rt] = mfma16(A[3], Bf2[3], acc2[rt]);
+              steps(2);
+              steps(3);
             }
           } else {
             auto dot_j = [&](auto jc) {
@@ -397,6 +420,7 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
           // this wave's reads of slot i % 2 are complete: refill it with block i + 2's tile
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0 (vmcnt, expcnt: no wait)
           xload(i + 2);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -410,7 +434,8 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       red[((wave * TH + 0) * RT + rt) * 64 + lane] = acc[rt];
-      if constexpr (TH == 2) red[((wave * TH + 1) * RT + rt) * 64 + lane] = acc2[rt];
+#pragma unroll
+      for (int q = 0; q + 1 < TH; ++q) red[((wave * TH + q + 1) * RT + rt) * 64 + lane] = accx[q][rt];
     }
     __syncthreads();
     auto sum = [&](int h, int rt, int l) {
@@ -484,7 +509,7 @@ constexpr int kNW = 8;  // waves per workgroup (K split)
 // unit that the slice allows.
 template <int RT, int XL, int KPW>
 constexpr int ring_depth() {
-  constexpr int d = XL == 32 ? 5 : XL >= 8 ? (RT >= 6 ? 2 : 5) : RT >= 2 ? 2 : (XL ? 5 : 3);
+  constexpr int d = XL >= 32 ? 5 : XL >= 8 ? (RT >= 6 ? 2 : 5) : RT >= 2 ? 2 : (XL ? 5 : 3);
   return d < KPW ? d : KPW;
 }
 
@@ -495,8 +520,9 @@ hipError_t run_k(const KArgs& a, hipStream_t stream) {
   const int nbc = nbw < KPW ? nbw : KPW;  // blocks per chunk
   const int xdim = XL >= 8 ? nbc : nbc * 128 + 8;
   size_t lds = XL == 32 ? (size_t)kNW * 2 * 32 * 256
+             : XL == 64 ? (size_t)kNW * 64 * 256
              : XL >= 8 ? (size_t)kNW * nbc * XL * 256 : XL == 4 ? (size_t)kNW * 4 * xdim * 2 : 0;
-  const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * (XL == 32 ? 2 : 1) * 64 * 16 : (size_t)kNW * RT * 64 * 4;
+  const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * (XL >= 32 ? XL / 16 : 1) * 64 * 16 : (size_t)kNW * RT * 64 * 4;
   if (red > lds) lds = red;
   constexpr int D = ring_depth<RT, XL, KPW>();
   if (a.K % 128)
@@ -534,10 +560,13 @@ hipError_t pick_rt(const KArgs& a, hipStream_t stream) {
     // the gate / up tiles of one pair; three pairs with a 16-row slice (one 160 KB workgroup
     // per compute unit: 17408-row pair, T = 16: 36.5 us against 37.6 with one pair)
     return run<BITS, MODE, XL == 16 ? 6 : 2, XL, EPI>(a, stream);
+  } else if constexpr (XL == 64 && BITS == 5) {
+    // (three row tiles of 5-bit codes with 64-token accumulators exceed the registers)
+    return run<BITS, MODE, 2, XL, EPI>(a, stream);
   } else if constexpr (XL >= 8) {
     // an 8-row slice (80 KB at K = 5120) leaves room for two workgroups per compute unit, a
-    // 16-row one for one: three row tiles each keep the tiles of a launch resident at once
-    // (batched 11264 x 5120, T = 8: 10.9 us against 11.6 us with two)
+    // 16-row one or a 32- / 64-row ring for one: three row tiles each keep the tiles of a
+    // launch resident at once (batched 11264 x 5120, T = 8: 10.9 us against 11.6 us with two)
     return run<BITS, MODE, 3, XL, EPI>(a, stream);
   } else {
     if (ntiles >= 4 * 256 * 2) return run<BITS, MODE, 2, XL, EPI>(a, stream);
@@ -583,10 +612,15 @@ hipError_t W4_PART_NAME(launch_stream16, W4_STREAM_BITS, W4_STREAM_EPI)(const KA
   return pick_xl<W4_STREAM_BITS, MODE_MFMA, W4_STREAM_EPI>(a, stream);
 }
 
-// 32-token mode (two-block ring of 32-row activation tiles): K <= 5120 only
+// 32- and 64-token modes (ring of 32- / 64-row activation tiles): K <= 5120 only
 hipError_t W4_PART_NAME(launch_stream32, W4_STREAM_BITS, W4_STREAM_EPI)(const KArgs& a, hipStream_t stream) {
   if ((a.KB + kNW - 1) / kNW > 5) return hipErrorInvalidValue;
   return pick_rt<W4_STREAM_BITS, MODE_MFMA, 32, W4_STREAM_EPI>(a, stream);
+}
+
+hipError_t W4_PART_NAME(launch_stream64, W4_STREAM_BITS, W4_STREAM_EPI)(const KArgs& a, hipStream_t stream) {
+  if ((a.KB + kNW - 1) / kNW > 5) return hipErrorInvalidValue;
+  return pick_rt<W4_STREAM_BITS, MODE_MFMA, 64, W4_STREAM_EPI>(a, stream);
 }
 
 }  // namespace w4

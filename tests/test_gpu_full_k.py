@@ -1,0 +1,60 @@
+"""GPU tier: the streaming kernel's activation slice and ring modes at the K where they hold all
+of a wave's k-blocks at once (K = 5120: five blocks per wave; K = 5056: the last block half
+empty), for both code widths and all three ops, against the fp64 oracle over every output.
+The route parity suite covers these modes at one or two blocks per wave; the full-size
+configuration tests cover 4-bit codes only.  N = 784 rows (49 tiles: the three-tile workgroups
+end on a partial one; the SwiGLU pair has 98 packed tiles)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4_groupwise_gemm_amd as w4
+from synth import make_weights, make_activations, make_residual
+from gpu_util import assert_close, canon, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+N = 784
+# route -> widths: 4-row slice, 8-row slice, 16-row slice, 32-row ring, 64-row ring
+CASES = [("mfma_stream_t16", t) for t in (4, 5, 8, 9, 16)] + [("mfma_stream_t32", t) for t in (17, 32)] + \
+        [("mfma_stream_t64", t) for t in (33, 64)]
+
+
+@pytest.mark.parametrize("K", [5120, 5056])
+@pytest.mark.parametrize("bits", [4, 5])
+@pytest.mark.parametrize("op", [w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD])
+def test_full_k_modes(K, bits, op):
+    rng = np.random.default_rng(K + 10 * bits + op)
+    scale = (0.0025, 0.01) if bits == 5 else (0.005, 0.02)
+    ws = [make_weights(rng, "w", N, K, bits, ("uniform", 6, 9), scale)]
+    if op == w4.OP_SWIGLU:
+        ws.append(make_weights(rng, "u", N, K, bits, ("uniform", 6, 9), scale))
+        pw = w4.pack_pair(canon(ws[0]), canon(ws[1]), bits, device=DEV)
+    else:
+        pw = w4.pack_weight(*canon(ws[0]), bits, device=DEV)
+    # activations as in the workloads: the SwiGLU pair's N(0, 0.5) without outlier channels,
+    # the single matrices' N(0, 1) with 8 channels scaled x30.  (With outliers the pair's
+    # fp16-rounded weights alone put single elements past the element bound, identically on
+    # every route: silu(gate) amplifies the up projection's rounding.)
+    swi = op == w4.OP_SWIGLU
+    x, _ = make_activations(rng, 64, K, 0.5 if swi else 1.0, 0 if swi else 8)
+    r = make_residual(rng, 64, N)
+    # one oracle call at 64 tokens: output row t depends on activation row t only
+    if op == w4.OP_SWIGLU:
+        ref64 = oracle.swiglu(x, canon(ws[0]), canon(ws[1]), bits=bits)
+    elif op == w4.OP_ADD:
+        ref64 = oracle.linear_add(x, *canon(ws[0]), r, bits=bits)
+    else:
+        ref64 = oracle.linear(x, *canon(ws[0]), bits=bits)
+    ids = {w4.route_name(i): i for i in range(w4.route_count())}
+    for route, T in CASES:
+        print(f"case full-k route={route} op={op} bits={bits} T={T} N={N} K={K}", flush=True)
+        xt = np.ascontiguousarray(x[:T])
+        rt = np.ascontiguousarray(r[:T])
+        y = w4.linear_route(ids[route], op, torch.from_numpy(xt).to(DEV), pw,
+                            residual=torch.from_numpy(rt).to(DEV) if op == w4.OP_ADD else None)
+        torch.cuda.synchronize()
+        assert_close(to_np(y), ref64[:T], f"{route} op{op} b{bits} T{T} K{K}")

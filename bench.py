@@ -300,6 +300,8 @@ def main() -> int:
         value = len(widths) * wstream_alg / (ms_per_step * 1e6)
         unit_v = "GB/s"
 
+    context = context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, dev)
+
     cpu, parity = None, None
     if not args.no_cpu_baseline:
         cpu, parity = cpu_baseline(wl, widths, op, bits, lo if not pair else None,
@@ -319,8 +321,93 @@ def main() -> int:
         "parity_ok": parity_ok, "parity": parity, "per_T": per_T,
         "roofline": roofline, "cpu_baseline": cpu,
     }
+    if context:
+        line["context"] = context
     print(json.dumps(line))
     return 1 if parity_ok is False else 0
+
+
+def context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, dev):
+    """Figures reported beside the measured path, never as its value.
+
+    * Parents that share one activation (the batched workload): each parent as a call of its
+      own and the sum of the two, beside the one N-concatenated call that per_T times.
+    * Prefill widths: a dense fp16 GEMM of the same shape through the vendor library (random
+      fp16 weights held as [K][N] for x @ W and as [N][K] for linear(x, W)), over rotated cold
+      weight copies: the ceiling a dequantising kernel is compared with.
+    Both timed over >= --cold-bytes of rotated copies, HIP events on the launch stream, median
+    of 5 (our calls replayed from a graph, the library's launched eagerly)."""
+    if args.route >= 0 or args.no_graph or pair:
+        return None
+    stream = torch.cuda.current_stream()
+
+    def timed(launch, copies, graph=True):
+        # graph: our own calls (capturable); eager for the vendor library, whose launches stay
+        # out of graphs here (a 80-280 us GEMM does not notice the launch gap)
+        for c in range(min(copies, 4)):
+            launch(c)
+        torch.cuda.synchronize()
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in range(copies):
+                    launch(c)
+            run = g.replay
+        else:
+            def run():
+                for c in range(copies):
+                    launch(c)
+        run()
+        torch.cuda.synchronize()
+        us = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3 / copies)
+        return float(np.median(us))
+
+    out = {}
+    if len(wl.weights) > 1 and op == w4.OP_LINEAR:
+        sep = {str(T): {} for T in widths}
+        for ws in wl.weights:
+            packed = w4.repack(ws.lo, ws.hi, ws.scales, ws.zeros, bits)
+            nbytes = sum(int(a.nbytes) for a in packed)
+            copies = max(2, int(np.ceil(args.cold_bytes * (1 << 30) / nbytes)))
+            pws = [w4.to_device(packed, ws.N, K, bits, False, device=dev) for _ in range(copies)]
+            for T in widths:
+                x = torch.from_numpy(np.ascontiguousarray(wl.x[:T])).to(dev)
+                y = torch.empty((T, ws.N), dtype=torch.float16, device=dev)
+                sep[str(T)][f"{ws.N}x{K}_us"] = timed(lambda c: w4.linear(x, pws[c], out=y), copies)
+            del pws
+        for T in widths:
+            d = sep[str(T)]
+            d["sum_us"] = float(sum(v for k, v in d.items() if k.endswith("_us")))
+            d["concatenated_us"] = per_T[str(T)]["us_mean"]
+        out["parents_as_separate_calls"] = sep
+    if min(widths) >= 1024:
+        wbytes = N * K * 2
+        copies = max(2, int(np.ceil(args.cold_bytes * (1 << 30) / wbytes)))
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(0)
+        # the two operand layouts a caller could hold: W as [K][N] (x @ W) and as [N][K]
+        # (linear(x, W) = x @ W^T, a plain 2-D fp16 product), both contiguous
+        wkn = [torch.randn((K, N), generator=gen, device=dev, dtype=torch.float16) for _ in range(copies)]
+        wnk = [torch.randn((N, K), generator=gen, device=dev, dtype=torch.float16) for _ in range(copies)]
+        dense = {}
+        for T in widths:
+            x = torch.from_numpy(np.ascontiguousarray(wl.x[:T])).to(dev)
+            us_kn = timed(lambda c: torch.matmul(x, wkn[c]), copies, graph=False)
+            us_nk = timed(lambda c: torch.nn.functional.linear(x, wnk[c]), copies, graph=False)
+            best = min(us_kn, us_nk)
+            dense[str(T)] = {"us_w_kn": us_kn, "us_w_nk": us_nk, "us_best": best,
+                             "TFLOPs_best": 2.0 * T * N * K / (best * 1e6)}
+        del wkn, wnk
+        out["dense_fp16_gemm_ceiling"] = {"what": "vendor-library fp16 GEMM (torch.matmul / linear) on random "
+                                                  "fp16 weights of the same shape, cold copies", "per_T": dense}
+    return out or None
 
 
 def route_sweep(args, w4, torch, widths, op, pws, xs, res, outs, copies, wstream_alg, N, K, rows,

@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256, OCC) void wide_kernel(KArgs a, int nrb, int nt
   if constexpr (NP == 5) {
     // Fifth pair: wave w holds the partial sums of k-steps (j, w/2), j in {2 (w%2), 2 (w%2)+1}
     // of every block.  The four are added in wave order through LDS (the activation buffers
-    // are free once every wave has left the loop); wave w finishes token tiles w*NTT/4 ...
+    // are free once every wave has left the loop); wave w finishes token tiles w, w + 4, ...
     static_assert(4 * NTT * 16 * 64 * 4 <= 2 * BN * 256, "reduction fits the activation buffers");
     float* red = reinterpret_cast<float*>(smem);
     __syncthreads();
@@ -303,9 +303,7 @@ __global__ __launch_bounds__(256, OCC) void wide_kernel(KArgs a, int nrb, int nt
 #pragma unroll
       for (int v = 0; v < 16; ++v) red[((wave * NTT + tt) * 16 + v) * 64 + lane] = accs[tt][v];
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NTT / 4; ++i) {
-      const int tt = wave * (NTT / 4) + i;
+    for (int tt = wave; tt < NTT; tt += 4) {
       f32x16 sum;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {

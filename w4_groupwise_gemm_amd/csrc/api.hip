@@ -19,7 +19,15 @@
 
 namespace {
 
-enum RouteKind { KIND_GEMV = 0, KIND_STREAM = 1, KIND_NARROW = 2, KIND_WIDE = 3, KIND_SPLITK = 4, KIND_STREAM32 = 5, KIND_STREAM64 = 6 };
+enum RouteKind {
+  KIND_GEMV = 0,
+  KIND_STREAM = 1,
+  KIND_NARROW = 2,
+  KIND_WIDE = 3,
+  KIND_SPLITK = 4,
+  KIND_STREAM32 = 5,
+  KIND_STREAM64 = 6
+};
 
 struct Route {
   const char* name;
@@ -40,7 +48,9 @@ const Route kRoutes[] = {
     {"mfma_stream_t64", 1, 64, KIND_STREAM64, 64},
 };
 constexpr int kNumRoutes = sizeof(kRoutes) / sizeof(kRoutes[0]);
-enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5, R_NTILED = 6, R_S32 = 7, R_S64 = 8 };
+// route ids (indices into kRoutes; R_N16 is the 16-token streaming route)
+enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5, R_NTILED = 6, R_S32 = 7,
+       R_S64 = 8 };
 
 constexpr int kMaxDim = 1 << 24;
 

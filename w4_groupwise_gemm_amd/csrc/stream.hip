@@ -1,5 +1,5 @@
-// Streaming path for small token counts: the GEMV route (exact T = 1..4, packed-fp16 dot
-// products) and the 16-token matrix-core route (T <= 16).
+// Streaming path for small and mid token counts: the GEMV route (exact T = 1..4, packed-fp16
+// dot products) and the matrix-core routes for T <= 16, <= 32 and <= 64 (16-token steps).
 //
 // Prior art: the SIMT split GEMVs and the Q4/Q5 small-T MMA kernels of the ninfer-3080
 // performance notes ("Why the round cost too much"; "What changed": permuted k order; "What
@@ -21,6 +21,11 @@
 //    registers), with 2 or 3 row tiles per workgroup since the slice then allows only one or
 //    two workgroups per compute unit; otherwise the 16-token activation fragments ride in the
 //    same ring as the codes;
+//  * for 17-64 tokens (K <= 5120) a whole slice no longer fits: each wave keeps a ring of
+//    32-row (two slots) or 64-row (one slot) activation tiles, refilled from memory as blocks
+//    are consumed, and feeds every dequantised weight fragment to 2 or 4 16-token steps; the
+//    waits count the loads issued after each tile, so scheduling barriers keep every tile
+//    load of the prologue ahead of the code loads;
 //  * the dequantisation is 13 vector ops per packed word when the zero-points of a block are
 //    integers (checked exactly, wave-uniformly, per block): mask-or the nibbles into the
 //    mantissa of fp16 1024 (one v_and_or_b32 per pair), subtract 1024 + z (or fold 1/16 and
@@ -128,8 +133,8 @@ struct Ring {
 // XL: token rows of the activation slice held in LDS (0: fragments in the ring instead; 4, 8
 // or 16; 32: a two-block ring of 32-row activation tiles, refilled as the blocks are consumed,
 // and two 16-token matrix-core steps per weight fragment; 64: one 64-row tile slot, refilled
-// with the next block's tile as soon as the current one has been read, and four steps).  xdim: XL = 4, fp16 elements per
-// slice row (padded); XL = 8 / 16, k-blocks of the slice.
+// with the next block's tile as soon as the current one has been read, and four steps).
+// xdim: XL = 4, fp16 elements per slice row (padded); XL = 8 / 16, k-blocks of the slice.
 // HB: K is not a multiple of 128, so the last k-block holds one group only (without it the
 // per-block test for that case, and its branches, compile away).
 template <int BITS, int MODE, int RT, int NW, int KPW, int D, int XL, int EPI, bool LOOP, bool HB>

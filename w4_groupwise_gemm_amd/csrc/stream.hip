@@ -303,24 +303,31 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
 
 #pragma unroll
     for (int i = 0; i < KPW; ++i) {
-      if (i + D < KPW && i + D < nb) issue(i + D);
+      // (ring modes issue every slot, re-reading a wave's last block past its end, so that the
+      // tile waits below can count the loads issued after each tile)
+      if (i + D < KPW && (RING || i + D < nb)) issue(i + D);
       if (i < nb) {
         const int kb = wave + NW * (cb + i);
         const bool half_block = HB && (kb * 128 + 64 >= a.K);
         // activation fragments of the block's four 32-k steps, read before the dequantisation
         // so that the LDS latency hides behind it (a half-empty last block skips steps 2, 3)
         f16x8 Bf[4], Bx[TH > 1 ? TH - 1 : 1][4];
-        if constexpr (XL == 32) {
-          // the ring tile of block i has landed once at most the loads issued after it are
-          // outstanding: the other blocks' codes (blocks 0, 1) and the next tile's refill
+        if constexpr (RING) {
+          // The ring tile of block i has landed once at most the loads issued after it are
+          // outstanding.  Issue order: tiles 0 (and 1 with two slots), code blocks 0 .. D-1;
+          // then code block i + D at the top of block i; the refill of tile i + 2 after block
+          // i's math (two slots) or of tile i + 1 right after block i's tile has been read (one
+          // slot).  CPB: code loads per block.
           constexpr int CPB = RT * (BITS == 5 ? 4 : 3);
-          wait_vmcnt_folded(i == 0 ? (KPW - 1) * CPB
-                                   : i == 1 ? (KPW - 2) * CPB + (2 < KPW ? 8 : 0) : (i + 1 < KPW ? 8 : 0));
-        } else if constexpr (XL == 64) {
-          // block 0's tile was issued before every code load; each later tile is the last load
-          // issued
-          constexpr int CPB = RT * (BITS == 5 ? 4 : 3);
-          wait_vmcnt_folded(i == 0 ? KPW * CPB : 0);
+          const int first = CPB * (D + (D < KPW ? 1 : 0));  // codes issued before block 0's wait
+          int n;
+          if constexpr (NSLOT == 2)
+            n = i == 0 ? first
+              : i == 1 ? 63  // (tile 1 was waited for with tile 0)
+              : CPB * (i - 1 + D < KPW) + 8 * (i + 1 < KPW) + CPB * (i + D < KPW);
+          else
+            n = i == 0 ? first : CPB * (i + D < KPW);
+          wait_vmcnt_folded(n);
         }
         if constexpr (MODE == MODE_MFMA) {
 #pragma unroll

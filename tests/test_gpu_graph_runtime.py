@@ -38,7 +38,7 @@ def _call(op, x, pw, r, out):
 
 
 @pytest.mark.parametrize("op", [w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD])
-@pytest.mark.parametrize("T", [1, 4, 16, 40, 200])
+@pytest.mark.parametrize("T", [1, 4, 16, 24, 40, 200])
 def test_graph_replays_match_eager(op, T):
     N, K, bits = 256, 1024, 4 if op != w4.OP_ADD else 5
     ws, pw, x, r = _setup(op, N, K, T, bits, seed=T + 10 * op)

@@ -336,7 +336,9 @@ def context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, de
     """Figures reported beside the measured path, never as its value.
 
     * Parents that share one activation (the batched workload): each parent as a call of its
-      own and the sum of the two, beside the one N-concatenated call that per_T times.
+      own and the sum of the two, beside the one N-concatenated call that per_T times; and the
+      two mixed-width (4-bit + 5-bit) input projections through the grouped call, beside the
+      same two matrices as two calls.
     * Prefill widths: a dense fp16 GEMM of the same shape through the vendor library (random
       fp16 weights held as [K][N] for x @ W and as [N][K] for linear(x, W)), over rotated cold
       weight copies: the ceiling a dequantising kernel is compared with.
@@ -392,6 +394,7 @@ def context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, de
             d["sum_us"] = float(sum(v for k, v in d.items() if k.endswith("_us")))
             d["concatenated_us"] = per_T[str(T)]["us_mean"]
         out["parents_as_separate_calls"] = sep
+        out["mixed_bits_parents"] = mixed_bits_parents(w4, torch, args, timed, K, dev)
     if min(widths) >= 1024:
         wbytes = N * K * 2
         copies = max(2, int(np.ceil(args.cold_bytes * (1 << 30) / wbytes)))
@@ -413,6 +416,43 @@ def context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, de
         out["dense_fp16_gemm_ceiling"] = {"what": "vendor-library fp16 GEMM (torch.matmul / linear) on random "
                                                   "fp16 weights of the same shape, cold copies", "per_T": dense}
     return out or None
+
+
+def mixed_bits_parents(w4, torch, args, timed, K, dev):
+    """The two mixed-width input projections of the hybrid model (GDN input: 4-bit 4096 rows +
+    5-bit 12288 rows; attention input: 4-bit 7168 + 5-bit 7168; K = 5120) at the widths the
+    one-launch grouped path covers: the grouped call against the two single-matrix calls
+    launched back to back, over rotated cold copies.  Weights follow the batched workload's
+    distribution for the 4-bit parent and the prefill workload's for the 5-bit one."""
+    from synth import make_weights, make_activations
+    from synth.inputs import CONFIGS
+    rng = np.random.default_rng(77)
+    x = torch.from_numpy(make_activations(rng, 16, K, 1.0, 8)[0]).to(dev)
+    res = {}
+    for name, specs in (("gdn_in", ((4096, 4), (12288, 5))), ("attn_in", ((7168, 4), (7168, 5)))):
+        packed = []
+        for i, (n, b) in enumerate(specs):
+            cfg = CONFIGS["batched" if b == 4 else "prefill"]
+            ws = make_weights(rng, f"{name}{i}", n, K, b, cfg["zero"], cfg["scale"])
+            packed.append(w4.repack(ws.lo, ws.hi, ws.scales, ws.zeros, b))
+        nbytes = sum(int(a.nbytes) for p in packed for a in p)
+        copies = max(2, int(np.ceil(args.cold_bytes * (1 << 30) / nbytes)))
+        pws = [[w4.to_device(p, n, K, b, False, device=dev) for p, (n, b) in zip(packed, specs)]
+               for _ in range(copies)]
+        per_T = {}
+        for T in (1, 4, 8, 16):
+            xt = x[:T].contiguous()
+            ys = [torch.empty((T, n), dtype=torch.float16, device=dev) for n, _ in specs]
+            g_us = timed(lambda c: w4.linear_grouped(xt, pws[c], outs=ys), copies)
+
+            def both(c):
+                for pw, y in zip(pws[c], ys):
+                    w4.linear(xt, pw, out=y)
+            s_us = timed(both, copies)
+            per_T[str(T)] = {"grouped_us": g_us, "two_calls_us": s_us, "saved_us": s_us - g_us}
+        res[name] = {"parents": [f"W{b} {n}x{K}" for n, b in specs], "per_T": per_T}
+        del pws
+    return res
 
 
 def route_sweep(args, w4, torch, widths, op, pws, xs, res, outs, copies, wstream_alg, N, K, rows,

@@ -130,6 +130,29 @@ int w4_linear_add(const uint16_t* x, const void* w, const uint16_t* scales, cons
                   const uint16_t* residual, int T, int N, int K, int bits, int group,
                   uint16_t* out, void* stream);
 
+/* ---- grouped call: several matrices that share one activation (ninfer-3080 performance notes,
+ * "What changed": two parents over one activation; the projections that read one activation
+ * with 4-bit and 5-bit weights).  One matrix of the group, as w4_repack output: */
+typedef struct {
+  const void* w;            /* packed codes of N rows x K columns */
+  const uint16_t* scales;   /* packed scales */
+  const uint16_t* zeros;    /* packed zero-points */
+  int N;                    /* rows (multiple of 16) */
+  int bits;                 /* 4 or 5; the matrices of a group may differ */
+  uint16_t* out;            /* fp16 [T][N], caller-owned, written (not read) */
+} w4_parent;
+
+#define W4_MAX_PARENTS 4
+
+/* out_p[T][N_p] = fp16_rne(X . dequant(W_p)^T) for p < nparents (1 .. W4_MAX_PARENTS), all
+ * reading x [T][K].  For T <= 16 and K <= 5120 one kernel launch covers every matrix (each
+ * workgroup runs the code width of its matrix); otherwise the call launches the route
+ * w4_route_for picks for each matrix, one after another on `stream`.  Validation as w4_linear
+ * for every matrix, and no output may overlap another matrix's output, packed data or x
+ * (W4_ERR_ALIAS).  parents: host array, read during the call only. */
+int w4_linear_grouped(const uint16_t* x, const w4_parent* parents, int nparents, int T, int K,
+                      int group, void* stream);
+
 /* ---- routes: every op has several kernels ("schedules"), each with an explicit T domain
  * (ninfer-3080 performance notes, "Route boundaries are measured here").  The three calls
  * above pick exactly one route with w4_route_for and launch it once. */

@@ -216,3 +216,28 @@ def test_repack_is_deterministic_and_validates():
     assert L.w4_repack(ptr, None, ptr, ptr, 16, 64, 4, 32, ptr, ptr, ptr) == -2
     assert L.w4_repack(ptr, None, ptr, ptr, 15, 64, 4, 64, ptr, ptr, ptr) == -1
     assert L.w4_repack(None, None, ptr, ptr, 16, 64, 4, 64, ptr, ptr, ptr) == -1
+
+
+# ---- grouped call: validation of every matrix and of overlaps between them (fake addresses)
+
+def _grouped(parents, T=4, K=512, x=0x10000, group=64):
+    arr = (w4._Parent * max(1, len(parents)))(*[w4._Parent(*p) for p in parents])
+    return w4.lib().w4_linear_grouped(x, arr if parents else None, len(parents), T, K, group, None)
+
+
+def test_grouped_validation():
+    a = (0x20000000, 0x30000000, 0x40000000, 256, 4, 0x50000000)
+    b = (0x21000000, 0x31000000, 0x41000000, 512, 5, 0x51000000)
+    # no GPU here: a valid group passes validation and stops at the device check
+    assert _grouped([a, b]) == -6
+    assert _grouped([]) == -1                      # no matrix
+    assert _grouped([a, b, a[:5] + (0x52000000,), b[:5] + (0x53000000,), a[:5] + (0x54000000,)]) == -1
+    assert _grouped([a, b[:4] + (3,) + b[5:]]) == -2                      # 3-bit codes
+    assert _grouped([a, b[:3] + (250,) + b[4:]]) == -1                    # N % 16
+    assert _grouped([a, b], K=500) == -1                                  # K % 64
+    assert _grouped([a, b], group=128) == -2
+    assert _grouped([a, b[:5] + (0x51000002,)]) == -3                     # misaligned output
+    assert _grouped([a, b[:5] + (0x50000000 + 64,)]) == -4                # outputs overlap
+    assert _grouped([a, b[:5] + (0x20000000 + 64,)]) == -4                # output over another's codes
+    assert _grouped([a, b[:5] + (0x10000 + 16,)]) == -4                   # output over x
+    assert _grouped([a, b], T=0) == 0                                     # T == 0: no-op

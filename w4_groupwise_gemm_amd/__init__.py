@@ -31,8 +31,14 @@ _STATUS = {0: "W4_OK", -1: "W4_ERR_INVALID_ARG", -2: "W4_ERR_UNSUPPORTED", -3: "
 EXPORTS = (
     "w4_packed_bytes", "w4_packed_sz_bytes", "w4_repack", "w4_repack_pair", "w4_linear",
     "w4_linear_swiglu", "w4_linear_add", "w4_route_for", "w4_linear_route", "w4_route_count",
-    "w4_route_name", "w4_route_domain", "w4_status_str", "w4_layout_version",
+    "w4_route_name", "w4_route_domain", "w4_status_str", "w4_layout_version", "w4_linear_grouped",
 )
+
+
+class _Parent(ctypes.Structure):
+    # mirrors w4_parent in include/w4gemm.h
+    _fields_ = [("w", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("zeros", ctypes.c_void_p),
+                ("N", ctypes.c_int), ("bits", ctypes.c_int), ("out", ctypes.c_void_p)]
 
 
 class W4Error(RuntimeError):
@@ -81,6 +87,8 @@ def lib() -> ctypes.CDLL:
     L.w4_status_str.argtypes = [i]
     L.w4_status_str.restype = ctypes.c_char_p
     L.w4_layout_version.argtypes = []
+    L.w4_linear_grouped.argtypes = [vp, ctypes.POINTER(_Parent), i, i, i, i, vp]
+    L.w4_linear_grouped.restype = i
     L.w4_layout_version.restype = i
     _lib = L
     return L
@@ -257,6 +265,24 @@ def linear_add(x, pw: PackedWeight, residual, out=None, stream=None):
                                _dptr(residual), T, pw.N, pw.K, pw.bits, GROUP, _dptr(out),
                                _stream(stream)), "w4_linear_add")
     return out
+
+
+def linear_grouped(x, pws, outs=None, stream=None):
+    """[x . dequant(W_p)^T for each packed matrix p] via ``w4_linear_grouped`` (1 to 4 matrices,
+    4- or 5-bit, same K, not SwiGLU pairs): one launch for T <= 16 and K <= 5120."""
+    pws = list(pws)
+    if not 1 <= len(pws) <= 4 or any(pw.pair for pw in pws) or len({pw.K for pw in pws}) != 1:
+        raise ValueError("linear_grouped takes 1 to 4 single matrices with one K")
+    K = pws[0].K
+    _check_x(x, K)
+    T = x.shape[0]
+    outs = [None] * len(pws) if outs is None else list(outs)
+    outs = [_out(o, T, pw.N, x) for o, pw in zip(outs, pws)]
+    arr = (_Parent * len(pws))(*[_Parent(_dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros), pw.N, pw.bits,
+                                         _dptr(o)) for pw, o in zip(pws, outs)])
+    _check(lib().w4_linear_grouped(_dptr(x), arr, len(pws), T, K, GROUP, _stream(stream)),
+           "w4_linear_grouped")
+    return outs
 
 
 def linear_route(route_id: int, op: int, x, pw: PackedWeight, residual=None, out=None,

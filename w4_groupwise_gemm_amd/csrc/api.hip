@@ -122,10 +122,8 @@ int device_check() {
 }
 
 // Boundaries from route sweeps on this chip (every route timed at the same T, cold weights, at
-// the decode, batched-decode, SwiGLU-pair and 5120-row prefill shapes): the streaming kernel
-// wins up to 10 tokens (SwiGLU pair: up to 16), the split-K kernel from 12 to 16 (16: 15.9 vs
-// 16.3 us at 11264 rows), the warp-specialised narrow kernels from 20 to 64 and, token-tiled,
-// beyond that while the wide kernel's grid is small; the wide kernel above.
+// the decode, batched-decode, SwiGLU-pair and 5120-row prefill shapes); the reasons are given
+// case by case below.
 int pick_route(int op, int bits, int T, int N, int K) {
   (void)bits;
   // The streaming route holds the activation slice of each wave in LDS up to K = 5120 (16 token
@@ -227,6 +225,64 @@ extern "C" int w4_linear_add(const uint16_t* x, const void* w, const uint16_t* s
                              const uint16_t* zeros, const uint16_t* residual, int T, int N, int K,
                              int bits, int group, uint16_t* out, void* stream) {
   return run_op(-1, W4_OP_ADD, x, w, scales, zeros, residual, T, N, K, bits, group, out, stream);
+}
+
+extern "C" int w4_linear_grouped(const uint16_t* x, const w4_parent* parents, int nparents, int T,
+                                 int K, int group, void* stream) {
+  if (!parents || nparents < 1 || nparents > W4_MAX_PARENTS) return W4_ERR_INVALID_ARG;
+  static_assert(W4_MAX_PARENTS == w4::kMaxParents, "one limit");
+  for (int p = 0; p < nparents; ++p) {
+    const w4_parent& q = parents[p];
+    const int st = validate(W4_OP_LINEAR, x, q.w, q.scales, q.zeros, nullptr, T, q.N, K, q.bits,
+                            group, q.out);
+    if (st != W4_OK) return st;
+  }
+  if (T == 0) return W4_OK;
+  // no output may overlap another matrix's output or inputs
+  auto rng = [](const void* ptr, size_t n) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(ptr);
+    return Range{b, b + n};
+  };
+  for (int p = 0; p < nparents; ++p) {
+    const Range ro = rng(parents[p].out, (size_t)T * parents[p].N * 2);
+    for (int q = 0; q < nparents; ++q) {
+      if (q == p) continue;
+      const w4_parent& o = parents[q];
+      const size_t szb = w4_packed_sz_bytes(o.N, K, group);
+      if (overlap(ro, rng(o.out, (size_t)T * o.N * 2)) || overlap(ro, rng(o.w, w4_packed_bytes(o.N, K, o.bits, group))) ||
+          overlap(ro, rng(o.scales, szb)) || overlap(ro, rng(o.zeros, szb)))
+        return W4_ERR_ALIAS;
+    }
+  }
+  const int st = device_check();
+  if (st != W4_OK) return st;
+  if (T <= 16 && K <= 5120) {
+    w4::GroupedArgs g;
+    g.n = nparents;
+    for (int p = 0; p < nparents; ++p) {
+      w4::KArgs& a = g.a[p];
+      a.x = reinterpret_cast<const _Float16*>(x);
+      a.w = static_cast<const uint8_t*>(parents[p].w);
+      a.sc = reinterpret_cast<const uint32_t*>(parents[p].scales);
+      a.zr = reinterpret_cast<const uint32_t*>(parents[p].zeros);
+      a.res = nullptr;
+      a.out = reinterpret_cast<_Float16*>(parents[p].out);
+      a.T = T;
+      a.rows = parents[p].N;
+      a.K = K;
+      a.KB = w4layout::num_kblocks(K);
+      a.ldo = parents[p].N;
+      g.bits[p] = parents[p].bits;
+    }
+    return w4::launch_grouped16(g, static_cast<hipStream_t>(stream)) == hipSuccess ? W4_OK : W4_ERR_LAUNCH;
+  }
+  for (int p = 0; p < nparents; ++p) {
+    const w4_parent& q = parents[p];
+    const int e = launch_route(pick_route(W4_OP_LINEAR, q.bits, T, q.N, K), W4_OP_LINEAR, x, q.w, q.scales,
+                               q.zeros, nullptr, T, q.N, K, q.bits, q.out, stream);
+    if (e != W4_OK) return e;
+  }
+  return W4_OK;
 }
 
 extern "C" int w4_route_for(int op, int bits, int T, int N, int K) {

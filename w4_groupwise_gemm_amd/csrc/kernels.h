@@ -20,8 +20,20 @@ struct KArgs {
   int ldo;               // output columns (N)
 };
 
+// Several matrices sharing one activation (same x, T and K), each with its own output.
+constexpr int kMaxParents = 4;
+struct GroupedArgs {
+  KArgs a[kMaxParents];   // per matrix: x, w, sc, zr, out, T, rows, K, KB, ldo (res unused)
+  int bits[kMaxParents];  // 4 or 5
+  int n;                  // 1 .. kMaxParents
+};
+
 // Each launcher enqueues exactly one kernel on `stream` and returns hipSuccess or the launch
 // error.  `epi` is one of w4dev::EPI_*.
+// streaming kernel over all matrices of a group in one launch (store epilogue; T <= 16,
+// K <= 5120); defined in the 4-bit store part of stream.hip
+hipError_t launch_grouped16(const GroupedArgs& g, hipStream_t stream);
+
 // streaming kernel (stream.hip, one object per code width b and epilogue e)
 #define W4_STREAM_PART(b, e)                                                    \
   hipError_t launch_gemv_b##b##_e##e(const KArgs& a, hipStream_t stream);     \

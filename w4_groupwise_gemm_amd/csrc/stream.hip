@@ -137,15 +137,16 @@ struct Ring {
 // xdim: XL = 4, fp16 elements per slice row (padded); XL = 8 / 16, k-blocks of the slice.
 // HB: K is not a multiple of 128, so the last k-block holds one group only (without it the
 // per-block test for that case, and its branches, compile away).
+// bx: the workgroup's index among those of this matrix (its row tiles are bx RT ..).
 template <int BITS, int MODE, int RT, int NW, int KPW, int D, int XL, int EPI, bool LOOP, bool HB>
-__global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
+__device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int BLK = block_bytes(BITS);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int ntiles = a.rows / 16;
-  const int tile0 = blockIdx.x * RT;
+  const int tile0 = bx * RT;
   // local block index c of this wave is k-block wave + NW * c; nbw of them
   const int nbw = wave < a.KB ? (a.KB - wave + NW - 1) / NW : 0;
   const int T = a.T;
@@ -508,6 +509,31 @@ __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
   }
 }
 
+template <int BITS, int MODE, int RT, int NW, int KPW, int D, int XL, int EPI, bool LOOP, bool HB>
+__global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
+  stream_body<BITS, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(a, xdim, blockIdx.x);
+}
+
+// Grouped launch: several matrices (4- or 5-bit) that share one activation, each with its own
+// output; workgroups [end[p-1], end[p]) run matrix p.
+struct GArgs {
+  KArgs a[kMaxParents];
+  int bits[kMaxParents];
+  int end[kMaxParents];  // exclusive prefix sums of the matrices' workgroup counts
+  int n;
+};
+
+template <int MODE, int RT, int NW, int KPW, int D, int XL, int EPI, bool LOOP, bool HB>
+__global__ __launch_bounds__(NW * 64) void stream_grouped_kernel(GArgs g, int xdim) {
+  int p = 0;
+  while (p + 1 < g.n && (int)blockIdx.x >= g.end[p]) ++p;
+  const int bx = blockIdx.x - (p > 0 ? g.end[p - 1] : 0);
+  if (g.bits[p] == 5)
+    stream_body<5, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(g.a[p], xdim, bx);
+  else
+    stream_body<4, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(g.a[p], xdim, bx);
+}
+
 constexpr int kNW = 8;  // waves per workgroup (K split)
 // Ring depth (k-blocks of loads in flight ahead of the math).  One row tile with the
 // activation slice in LDS: 5, every block of a 5120-column wave in flight at once (decode
@@ -634,5 +660,61 @@ hipError_t W4_PART_NAME(launch_stream64, W4_STREAM_BITS, W4_STREAM_EPI)(const KA
   if ((a.KB + kNW - 1) / kNW > 5) return hipErrorInvalidValue;
   return pick_rt<W4_STREAM_BITS, MODE_MFMA, 64, W4_STREAM_EPI>(a, stream);
 }
+
+#if W4_STREAM_BITS == 4 && W4_STREAM_EPI == 0
+// Grouped launch (both code widths are compiled here).  The slice mode and the tiles per
+// workgroup follow the single-matrix choice for the same T at K <= 5120: a 4-row slice with
+// one tile (T <= 4), an 8- or 16-row slice with three.
+namespace {
+template <int RT, int XL, int KPW>
+hipError_t run_grouped_k(const GroupedArgs& ga, hipStream_t stream) {
+  GArgs g;
+  g.n = ga.n;
+  int total = 0;
+  for (int p = 0; p < ga.n; ++p) {
+    g.a[p] = ga.a[p];
+    g.bits[p] = ga.bits[p];
+    total += (ga.a[p].rows / 16 + RT - 1) / RT;
+    g.end[p] = total;
+  }
+  const KArgs& a = ga.a[0];
+  const int nbw = (a.KB + kNW - 1) / kNW;
+  const int nbc = nbw < KPW ? nbw : KPW;
+  const int xdim = XL >= 8 ? nbc : nbc * 128 + 8;
+  size_t lds = XL >= 8 ? (size_t)kNW * nbc * XL * 256 : (size_t)kNW * 4 * xdim * 2;
+  const size_t red = (size_t)kNW * RT * 64 * 16;
+  if (red > lds) lds = red;
+  constexpr int D = ring_depth<RT, XL, KPW>();
+  if (a.K % 128)
+    hipLaunchKernelGGL((stream_grouped_kernel<MODE_MFMA, RT, kNW, KPW, D, XL, EPI_STORE, false, true>),
+                       dim3(total), dim3(kNW * 64), lds, stream, g, xdim);
+  else
+    hipLaunchKernelGGL((stream_grouped_kernel<MODE_MFMA, RT, kNW, KPW, D, XL, EPI_STORE, false, false>),
+                       dim3(total), dim3(kNW * 64), lds, stream, g, xdim);
+  return hipGetLastError();
+}
+
+template <int RT, int XL>
+hipError_t run_grouped(const GroupedArgs& ga, hipStream_t stream) {
+  switch ((ga.a[0].KB + kNW - 1) / kNW) {
+    case 1: return run_grouped_k<RT, XL, 1>(ga, stream);
+    case 2: return run_grouped_k<RT, XL, 2>(ga, stream);
+    case 3: return run_grouped_k<RT, XL, 3>(ga, stream);
+    case 4: return run_grouped_k<RT, XL, 4>(ga, stream);
+    case 5: return run_grouped_k<RT, XL, 5>(ga, stream);
+    default: return hipErrorInvalidValue;  // K <= 5120 only
+  }
+}
+}  // namespace
+
+hipError_t launch_grouped16(const GroupedArgs& ga, hipStream_t stream) {
+  if (ga.n < 1 || ga.n > kMaxParents) return hipErrorInvalidValue;
+  const int T = ga.a[0].T;
+  if (T < 1 || T > 16) return hipErrorInvalidValue;
+  if (T <= 4) return run_grouped<1, 4>(ga, stream);
+  if (T <= 8) return run_grouped<3, 8>(ga, stream);
+  return run_grouped<3, 16>(ga, stream);
+}
+#endif
 
 }  // namespace w4

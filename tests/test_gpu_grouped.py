@@ -4,7 +4,9 @@ for that matrix (same kernels, same summation order), and match the fp64 oracle.
 span ragged row tiles, a half k-block (K % 128 == 64) and every slice mode of the one-launch
 path (T <= 4, 5..8, 9..16) plus widths above it (one launch per matrix); the full-size cases
 are the two mixed-width input projections of the hybrid model the measurements come from
-(4-bit 4096 + 5-bit 12288, 4-bit 7168 + 5-bit 7168, K = 5120), checked on sampled columns."""
+(4-bit 4096 + 5-bit 12288, 4-bit 7168 + 5-bit 7168, K = 5120) and the batched workload's two
+4-bit parents, checked on sampled columns; between them they take both row-tile counts of the
+one-launch path at T = 5..16."""
 from __future__ import annotations
 
 import numpy as np
@@ -66,7 +68,9 @@ def test_grouped_repeat_and_stream_order():
             assert np.array_equal(to_np(y).view(np.uint16), to_np(r).view(np.uint16)), T
 
 
-FULL = [((4096, 4), (12288, 5)), ((7168, 4), (7168, 5))]
+# the two mixed-width projections (two row tiles per workgroup at T = 5..16: 512 and 448
+# workgroups) and the batched workload's two 4-bit parents as a group (three row tiles: 236)
+FULL = [((4096, 4), (12288, 5)), ((7168, 4), (7168, 5)), ((7168, 4), (4096, 4))]
 
 
 @pytest.mark.parametrize("T", [1, 4, 8, 16])

@@ -545,6 +545,66 @@ constexpr int kNW = 8;  // waves per workgroup (K split)
 // than the chunk.  Three row tiles with an 8- or 16-row slice: likewise 5.  Six row tiles (the
 // SwiGLU pair with a 16-row slice): 2, within the registers of the one workgroup per compute
 // unit that the slice allows.
+// Row tiles per workgroup where a launch holds about one round of workgroups (the 8- and
+// 16-row slices and the 32- / 64-row rings, which allow two or one workgroups per compute unit).
+// Workgroups are taken round-robin over the 256 compute units in launch order; a compute unit's
+// cost is the code bits of the row tiles it runs, plus a start-up cost per workgroup (its
+// activation slice or ring prologue and its final reduction): half a 4-bit tile with a slice,
+// a tile and a half with a ring, which also allows only one workgroup per compute unit at a
+// time.  The count (1 .. max_rt) with the smallest largest cost wins; ties go to more tiles
+// (fewer workgroups).  Measured at K = 5120 (us; one, two, three row tiles per workgroup):
+//   4-bit  4096 rows: T = 8   5.4 /  7.1 /  8.4    T = 32  7.6 /  9.0 / 10.9   (one wins)
+//   4-bit  7168 rows: T = 16 10.0 /  8.3 /  9.7    T = 32 13.1 / 10.2 / 11.6   (two)
+//   4-bit 11264 rows: T = 16 14.5 / 14.4 / 11.1    T = 64 27.4 / 24.4 / 18.1   (three)
+//   5-bit 12288 rows: T = 16 17.3 / 17.1 / 14.1    T = 32 21.7 / 20.9 / 16.8   (three)
+//   5-bit 12288 rows, T = 64 (at most two: see pick_rt): 29.5 / 27.4                (two)
+// and for the groups of the grouped launch (4-bit 4096 + 5-bit 12288 rows, T = 8: 16.0 / 15.1 /
+// 20.1 us; two).
+struct TileGroup {
+  int tiles;  // 16-row tiles of one matrix
+  int bits;   // its code width
+};
+
+inline int launch_cost(const TileGroup* m, int n, int rt, int start) {
+  constexpr int kCUs = 256;
+  if (n == 1) {  // one matrix: the busiest compute unit runs ceil(workgroups / 256) of them
+    const int nwg = (m[0].tiles + rt - 1) / rt;
+    return (rt * m[0].bits + start) * ((nwg + kCUs - 1) / kCUs);
+  }
+  int first = 0;  // index of the matrix's first workgroup in the launch
+  int worst = 0;
+  int cost[kCUs] = {};
+  for (int p = 0; p < n; ++p) {
+    const int nwg = (m[p].tiles + rt - 1) / rt;
+    const int w = rt * m[p].bits + start;
+    // workgroups first .. first + nwg - 1 land on compute units (first + i) % 256
+    const int full = nwg / kCUs, rest = nwg % kCUs;
+    for (int c = 0; c < kCUs; ++c) {
+      const int extra = ((c - first % kCUs + kCUs) % kCUs) < rest ? 1 : 0;
+      cost[c] += w * (full + extra);
+    }
+    first += nwg;
+  }
+  for (int c = 0; c < kCUs; ++c) worst = cost[c] > worst ? cost[c] : worst;
+  return worst;
+}
+
+// start: the start-up cost per workgroup, in bits of one 16-row tile (2 with an activation
+// slice, 6 with a ring)
+inline int tiles_per_workgroup(const TileGroup* m, int n, int max_rt, int start) {
+  int best = max_rt, best_cost = launch_cost(m, n, max_rt, start);
+  for (int rt = max_rt - 1; rt >= 1; --rt) {
+    const int c = launch_cost(m, n, rt, start);
+    if (c < best_cost) best = rt, best_cost = c;
+  }
+  return best;
+}
+
+inline int tiles_per_workgroup(int ntiles, int bits, int max_rt, int start) {
+  const TileGroup m{ntiles, bits};
+  return tiles_per_workgroup(&m, 1, max_rt, start);
+}
+
 template <int RT, int XL, int KPW>
 constexpr int ring_depth() {
   constexpr int d = XL >= 32 ? 5 : XL >= 8 ? (RT >= 6 ? 2 : 5) : RT >= 2 ? 2 : (XL ? 5 : 3);
@@ -598,14 +658,17 @@ hipError_t pick_rt(const KArgs& a, hipStream_t stream) {
     // the gate / up tiles of one pair; three pairs with a 16-row slice (one 160 KB workgroup
     // per compute unit: 17408-row pair, T = 16: 36.5 us against 37.6 with one pair)
     return run<BITS, MODE, XL == 16 ? 6 : 2, XL, EPI>(a, stream);
-  } else if constexpr (XL == 64 && BITS == 5) {
-    // (three row tiles of 5-bit codes with 64-token accumulators exceed the registers)
-    return run<BITS, MODE, 2, XL, EPI>(a, stream);
   } else if constexpr (XL >= 8) {
     // an 8-row slice (80 KB at K = 5120) leaves room for two workgroups per compute unit, a
-    // 16-row one or a 32- / 64-row ring for one: three row tiles each keep the tiles of a
-    // launch resident at once (batched 11264 x 5120, T = 8: 10.9 us against 11.6 us with two)
-    return run<BITS, MODE, 3, XL, EPI>(a, stream);
+    // 16-row one or a 32- / 64-row ring for one, so the row tiles per workgroup decide how
+    // evenly a launch spreads over the compute units (tiles_per_workgroup); three row tiles of
+    // 5-bit codes with 64-token accumulators exceed the registers
+    const int rt = tiles_per_workgroup(ntiles, BITS, XL == 64 && BITS == 5 ? 2 : 3, XL >= 32 ? 6 : 2);
+    if (rt == 1) return run<BITS, MODE, 1, XL, EPI>(a, stream);
+    if constexpr (!(XL == 64 && BITS == 5)) {
+      if (rt == 3) return run<BITS, MODE, 3, XL, EPI>(a, stream);
+    }
+    return run<BITS, MODE, 2, XL, EPI>(a, stream);
   } else {
     if (ntiles >= 4 * 256 * 2) return run<BITS, MODE, 2, XL, EPI>(a, stream);
     return run<BITS, MODE, 1, XL, EPI>(a, stream);
@@ -662,9 +725,10 @@ hipError_t W4_PART_NAME(launch_stream64, W4_STREAM_BITS, W4_STREAM_EPI)(const KA
 }
 
 #if W4_STREAM_BITS == 4 && W4_STREAM_EPI == 0
-// Grouped launch (both code widths are compiled here).  The slice mode and the tiles per
-// workgroup follow the single-matrix choice for the same T at K <= 5120: a 4-row slice with
-// one tile (T <= 4), an 8- or 16-row slice with three.
+// Grouped launch (both code widths are compiled here).  The slice mode follows the
+// single-matrix choice for the same T at K <= 5120 (4 rows at T <= 4, else 8 or 16), so every
+// output is bit-identical to the single-matrix call's; the row tiles per workgroup are chosen
+// for the group as a whole (launch_grouped16).
 namespace {
 template <int RT, int XL, int KPW>
 hipError_t run_grouped_k(const GroupedArgs& ga, hipStream_t stream) {
@@ -705,15 +769,28 @@ hipError_t run_grouped(const GroupedArgs& ga, hipStream_t stream) {
     default: return hipErrorInvalidValue;  // K <= 5120 only
   }
 }
+
 }  // namespace
 
+// Row tiles per workgroup: at T <= 4 one (as the single-matrix route); with an 8- or 16-row
+// slice the count tiles_per_workgroup picks for the group as a whole.  A group's matrices
+// rarely divide into whole rounds the way one matrix does: 4-bit 4096 + 5-bit 12288 rows with
+// three tiles is 342 workgroups, so 86 compute units run two and the launch waits for them
+// (T = 8: 20.1 us), while two tiles make 512, two per compute unit (15.1 us).
 hipError_t launch_grouped16(const GroupedArgs& ga, hipStream_t stream) {
   if (ga.n < 1 || ga.n > kMaxParents) return hipErrorInvalidValue;
   const int T = ga.a[0].T;
   if (T < 1 || T > 16) return hipErrorInvalidValue;
   if (T <= 4) return run_grouped<1, 4>(ga, stream);
-  if (T <= 8) return run_grouped<3, 8>(ga, stream);
-  return run_grouped<3, 16>(ga, stream);
+  TileGroup m[kMaxParents];
+  for (int p = 0; p < ga.n; ++p) m[p] = TileGroup{ga.a[p].rows / 16, ga.bits[p]};
+  const int rt = tiles_per_workgroup(m, ga.n, 3, 2);
+  if (T <= 8) {
+    if (rt == 1) return run_grouped<1, 8>(ga, stream);
+    return rt == 2 ? run_grouped<2, 8>(ga, stream) : run_grouped<3, 8>(ga, stream);
+  }
+  if (rt == 1) return run_grouped<1, 16>(ga, stream);
+  return rt == 2 ? run_grouped<2, 16>(ga, stream) : run_grouped<3, 16>(ga, stream);
 }
 #endif
 

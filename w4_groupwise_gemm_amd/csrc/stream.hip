@@ -655,9 +655,20 @@ template <int BITS, int MODE, int XL, int EPI>
 hipError_t pick_rt(const KArgs& a, hipStream_t stream) {
   const int ntiles = a.rows / 16;
   if constexpr (EPI == EPI_SWIGLU) {
-    // the gate / up tiles of one pair; three pairs with a 16-row slice (one 160 KB workgroup
-    // per compute unit: 17408-row pair, T = 16: 36.5 us against 37.6 with one pair)
-    return run<BITS, MODE, XL == 16 ? 6 : 2, XL, EPI>(a, stream);
+    // the gate / up tiles of one pair.  With a 16-row slice (one 160 KB workgroup per compute
+    // unit) one or three pairs, by the balance rule with a start-up cost of a tile and a half
+    // per workgroup: 17408-row pair, T = 16: 33.0 us with three against 35.4 with one; 8192
+    // rows 17.0 against 16.1; 4096 rows (86 workgroups with three) 15.6 against 8.7.
+    // Otherwise one pair (every other width and size measured best so, e.g. 17408 rows, T = 8:
+    // 24.7 against 32.2 us with three).
+    if constexpr (XL == 16) {
+      const TileGroup m{ntiles, BITS};
+      if (launch_cost(&m, 1, 2, 6) < launch_cost(&m, 1, 6, 6))
+        return run<BITS, MODE, 2, XL, EPI>(a, stream);
+      return run<BITS, MODE, 6, XL, EPI>(a, stream);
+    } else {
+      return run<BITS, MODE, 2, XL, EPI>(a, stream);
+    }
   } else if constexpr (XL >= 8) {
     // an 8-row slice (80 KB at K = 5120) leaves room for two workgroups per compute unit, a
     // 16-row one or a 32- / 64-row ring for one, so the row tiles per workgroup decide how

@@ -420,14 +420,14 @@ def context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, de
 
 def mixed_bits_parents(w4, torch, args, timed, K, dev):
     """The two mixed-width input projections of the hybrid model (GDN input: 4-bit 4096 rows +
-    5-bit 12288 rows; attention input: 4-bit 7168 + 5-bit 7168; K = 5120) at the widths the
-    one-launch grouped path covers: the grouped call against the two single-matrix calls
-    launched back to back, over rotated cold copies.  Weights follow the batched workload's
+    5-bit 12288 rows; attention input: 4-bit 7168 + 5-bit 7168; K = 5120) at widths across the
+    one-launch grouped path: the grouped call against the two single-matrix calls launched
+    back to back, over rotated cold copies.  Weights follow the batched workload's
     distribution for the 4-bit parent and the prefill workload's for the 5-bit one."""
     from synth import make_weights, make_activations
     from synth.inputs import CONFIGS
     rng = np.random.default_rng(77)
-    x = torch.from_numpy(make_activations(rng, 16, K, 1.0, 8)[0]).to(dev)
+    x = torch.from_numpy(make_activations(rng, 64, K, 1.0, 8)[0]).to(dev)
     res = {}
     for name, specs in (("gdn_in", ((4096, 4), (12288, 5))), ("attn_in", ((7168, 4), (7168, 5)))):
         packed = []
@@ -440,7 +440,7 @@ def mixed_bits_parents(w4, torch, args, timed, K, dev):
         pws = [[w4.to_device(p, n, K, b, False, device=dev) for p, (n, b) in zip(packed, specs)]
                for _ in range(copies)]
         per_T = {}
-        for T in (1, 4, 8, 16):
+        for T in (1, 4, 8, 16, 32, 64):
             xt = x[:T].contiguous()
             ys = [torch.empty((T, n), dtype=torch.float16, device=dev) for n, _ in specs]
             g_us = timed(lambda c: w4.linear_grouped(xt, pws[c], outs=ys), copies)

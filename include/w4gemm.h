@@ -145,7 +145,7 @@ typedef struct {
 #define W4_MAX_PARENTS 4
 
 /* out_p[T][N_p] = fp16_rne(X . dequant(W_p)^T) for p < nparents (1 .. W4_MAX_PARENTS), all
- * reading x [T][K].  For T <= 16 and K <= 5120 one kernel launch covers every matrix (each
+ * reading x [T][K].  For T <= 64 and K <= 5120 one kernel launch covers every matrix (each
  * workgroup runs the code width of its matrix); otherwise the call launches the route
  * w4_route_for picks for each matrix, one after another on `stream`.  Validation as w4_linear
  * for every matrix, and no output may overlap another matrix's output, packed data or x

@@ -1,12 +1,13 @@
 """GPU tier: the grouped call (several packed matrices, 4- or 5-bit, over one activation, each
 with its own output).  Each output must equal, bit for bit, what the single-matrix call gives
 for that matrix (same kernels, same summation order), and match the fp64 oracle.  Small shapes
-span ragged row tiles, a half k-block (K % 128 == 64) and every slice mode of the one-launch
-path (T <= 4, 5..8, 9..16) plus widths above it (one launch per matrix); the full-size cases
+span ragged row tiles, a half k-block (K % 128 == 64) and every slice and ring mode of the
+one-launch path (T <= 4, 5..8, 9..16, 17..32, 33..64) plus a width above it (one launch per
+matrix); the full-size cases
 are the two mixed-width input projections of the hybrid model the measurements come from
 (4-bit 4096 + 5-bit 12288, 4-bit 7168 + 5-bit 7168, K = 5120) and the batched workload's two
-4-bit parents, checked on sampled columns; between them they take both row-tile counts of the
-one-launch path at T = 5..16."""
+4-bit parents, checked on sampled columns; between them they take one, two and three row tiles
+per workgroup."""
 from __future__ import annotations
 
 import numpy as np
@@ -33,7 +34,7 @@ def _weights(rng, specs, K):
 SMALL = [((272, 4), (400, 5), (96, 4)), ((128, 5),), ((64, 4), (48, 5), (32, 4), (16, 5))]
 
 
-@pytest.mark.parametrize("T", [1, 3, 4, 5, 8, 9, 16, 17, 40])
+@pytest.mark.parametrize("T", [1, 3, 4, 5, 8, 9, 16, 17, 24, 32, 33, 40, 64, 65])
 @pytest.mark.parametrize("K", [704, 5120])
 @pytest.mark.parametrize("specs", SMALL, ids=lambda s: "+".join(f"{n}b{b}" for n, b in s))
 def test_grouped_matches_single_and_oracle(specs, K, T):
@@ -58,7 +59,7 @@ def test_grouped_repeat_and_stream_order():
     K = 1024
     ws = _weights(rng, ((320, 4), (160, 5)), K)
     pws = [w4.pack_weight(*canon(w), b, device=DEV) for w, b in zip(ws, (4, 5))]
-    for T in (16, 2, 7, 1, 12):
+    for T in (16, 2, 7, 1, 12, 40, 20):
         x, _ = make_activations(rng, T, K, 1.0, 0)
         xd = torch.from_numpy(x).to(DEV)
         ys = w4.linear_grouped(xd, pws[::-1] if T % 2 else pws)
@@ -73,7 +74,7 @@ def test_grouped_repeat_and_stream_order():
 FULL = [((4096, 4), (12288, 5)), ((7168, 4), (7168, 5)), ((7168, 4), (4096, 4))]
 
 
-@pytest.mark.parametrize("T", [1, 4, 8, 16])
+@pytest.mark.parametrize("T", [1, 4, 8, 16, 32, 64])
 @pytest.mark.parametrize("specs", FULL, ids=lambda s: "+".join(f"{n}b{b}" for n, b in s))
 def test_grouped_full_size(specs, T):
     K = 5120

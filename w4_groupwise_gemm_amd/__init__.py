@@ -269,7 +269,7 @@ def linear_add(x, pw: PackedWeight, residual, out=None, stream=None):
 
 def linear_grouped(x, pws, outs=None, stream=None):
     """[x . dequant(W_p)^T for each packed matrix p] via ``w4_linear_grouped`` (1 to 4 matrices,
-    4- or 5-bit, same K, not SwiGLU pairs): one launch for T <= 16 and K <= 5120."""
+    4- or 5-bit, same K, not SwiGLU pairs): one launch for T <= 64 and K <= 5120."""
     pws = list(pws)
     if not 1 <= len(pws) <= 4 or any(pw.pair for pw in pws) or len({pw.K for pw in pws}) != 1:
         raise ValueError("linear_grouped takes 1 to 4 single matrices with one K")

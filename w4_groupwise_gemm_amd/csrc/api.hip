@@ -256,7 +256,7 @@ extern "C" int w4_linear_grouped(const uint16_t* x, const w4_parent* parents, in
   }
   const int st = device_check();
   if (st != W4_OK) return st;
-  if (T <= 16 && K <= 5120) {
+  if (T <= 64 && K <= 5120) {
     w4::GroupedArgs g;
     g.n = nparents;
     for (int p = 0; p < nparents; ++p) {
@@ -274,7 +274,7 @@ extern "C" int w4_linear_grouped(const uint16_t* x, const w4_parent* parents, in
       a.ldo = parents[p].N;
       g.bits[p] = parents[p].bits;
     }
-    return w4::launch_grouped16(g, static_cast<hipStream_t>(stream)) == hipSuccess ? W4_OK : W4_ERR_LAUNCH;
+    return w4::launch_grouped(g, static_cast<hipStream_t>(stream)) == hipSuccess ? W4_OK : W4_ERR_LAUNCH;
   }
   for (int p = 0; p < nparents; ++p) {
     const w4_parent& q = parents[p];

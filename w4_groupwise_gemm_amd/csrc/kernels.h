@@ -30,9 +30,9 @@ struct GroupedArgs {
 
 // Each launcher enqueues exactly one kernel on `stream` and returns hipSuccess or the launch
 // error.  `epi` is one of w4dev::EPI_*.
-// streaming kernel over all matrices of a group in one launch (store epilogue; T <= 16,
+// streaming kernel over all matrices of a group in one launch (store epilogue; T <= 64,
 // K <= 5120); defined in the 4-bit store part of stream.hip
-hipError_t launch_grouped16(const GroupedArgs& g, hipStream_t stream);
+hipError_t launch_grouped(const GroupedArgs& g, hipStream_t stream);
 
 // streaming kernel (stream.hip, one object per code width b and epilogue e)
 #define W4_STREAM_PART(b, e)                                                    \

@@ -611,17 +611,25 @@ constexpr int ring_depth() {
   return d < KPW ? d : KPW;
 }
 
+// Dynamic LDS of one workgroup: the activation slice or ring (nbc blocks per chunk; xdim as
+// passed to the kernel), or the final reduction of the NW partial sums if that is larger.
+template <int MODE, int RT, int XL>
+size_t stream_lds(int nbc, int xdim) {
+  const size_t x = XL == 32 ? (size_t)kNW * 2 * 32 * 256
+                 : XL == 64 ? (size_t)kNW * 64 * 256
+                 : XL >= 8 ? (size_t)kNW * nbc * XL * 256 : XL == 4 ? (size_t)kNW * 4 * xdim * 2 : 0;
+  const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * (XL >= 32 ? XL / 16 : 1) * 64 * 16
+                                       : (size_t)kNW * RT * 64 * 4;
+  return red > x ? red : x;
+}
+
 template <int BITS, int MODE, int RT, int XL, int EPI, int KPW, bool LOOP>
 hipError_t run_k(const KArgs& a, hipStream_t stream) {
   const int ntiles = a.rows / 16;
   const int nbw = (a.KB + kNW - 1) / kNW;
   const int nbc = nbw < KPW ? nbw : KPW;  // blocks per chunk
   const int xdim = XL >= 8 ? nbc : nbc * 128 + 8;
-  size_t lds = XL == 32 ? (size_t)kNW * 2 * 32 * 256
-             : XL == 64 ? (size_t)kNW * 64 * 256
-             : XL >= 8 ? (size_t)kNW * nbc * XL * 256 : XL == 4 ? (size_t)kNW * 4 * xdim * 2 : 0;
-  const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * (XL >= 32 ? XL / 16 : 1) * 64 * 16 : (size_t)kNW * RT * 64 * 4;
-  if (red > lds) lds = red;
+  const size_t lds = stream_lds<MODE, RT, XL>(nbc, xdim);
   constexpr int D = ring_depth<RT, XL, KPW>();
   if (a.K % 128)
     hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, D, XL, EPI, LOOP, true>),
@@ -736,10 +744,10 @@ hipError_t W4_PART_NAME(launch_stream64, W4_STREAM_BITS, W4_STREAM_EPI)(const KA
 }
 
 #if W4_STREAM_BITS == 4 && W4_STREAM_EPI == 0
-// Grouped launch (both code widths are compiled here).  The slice mode follows the
-// single-matrix choice for the same T at K <= 5120 (4 rows at T <= 4, else 8 or 16), so every
-// output is bit-identical to the single-matrix call's; the row tiles per workgroup are chosen
-// for the group as a whole (launch_grouped16).
+// Grouped launch (both code widths are compiled here).  The slice or ring mode follows the
+// single-matrix choice for the same T at K <= 5120 (a 4-, 8- or 16-row slice up to 16 tokens,
+// the 32- or 64-row ring up to 64), so every output is bit-identical to the single-matrix
+// call's; the row tiles per workgroup are chosen for the group as a whole (launch_grouped).
 namespace {
 template <int RT, int XL, int KPW>
 hipError_t run_grouped_k(const GroupedArgs& ga, hipStream_t stream) {
@@ -756,9 +764,7 @@ hipError_t run_grouped_k(const GroupedArgs& ga, hipStream_t stream) {
   const int nbw = (a.KB + kNW - 1) / kNW;
   const int nbc = nbw < KPW ? nbw : KPW;
   const int xdim = XL >= 8 ? nbc : nbc * 128 + 8;
-  size_t lds = XL >= 8 ? (size_t)kNW * nbc * XL * 256 : (size_t)kNW * 4 * xdim * 2;
-  const size_t red = (size_t)kNW * RT * 64 * 16;
-  if (red > lds) lds = red;
+  const size_t lds = stream_lds<MODE_MFMA, RT, XL>(nbc, xdim);
   constexpr int D = ring_depth<RT, XL, KPW>();
   if (a.K % 128)
     hipLaunchKernelGGL((stream_grouped_kernel<MODE_MFMA, RT, kNW, KPW, D, XL, EPI_STORE, false, true>),
@@ -783,25 +789,36 @@ hipError_t run_grouped(const GroupedArgs& ga, hipStream_t stream) {
 
 }  // namespace
 
-// Row tiles per workgroup: at T <= 4 one (as the single-matrix route); with an 8- or 16-row
-// slice the count tiles_per_workgroup picks for the group as a whole.  A group's matrices
-// rarely divide into whole rounds the way one matrix does: 4-bit 4096 + 5-bit 12288 rows with
-// three tiles is 342 workgroups, so 86 compute units run two and the launch waits for them
-// (T = 8: 20.1 us), while two tiles make 512, two per compute unit (15.1 us).
-hipError_t launch_grouped16(const GroupedArgs& ga, hipStream_t stream) {
+// Row tiles per workgroup: at T <= 4 one (as the single-matrix route); otherwise the count
+// tiles_per_workgroup picks for the group as a whole, with the start-up cost of a slice or of a
+// ring, and at most two with the 64-row ring (whose 5-bit body, compiled into the same kernel,
+// cannot hold three tiles' accumulators).  A group's matrices rarely divide into whole rounds
+// the way one matrix does: 4-bit 4096 + 5-bit 12288 rows with three tiles is 342 workgroups, so
+// 86 compute units run two and the launch waits for them (T = 8: 20.1 us), while two tiles make
+// 512, two per compute unit (15.1 us).
+hipError_t launch_grouped(const GroupedArgs& ga, hipStream_t stream) {
   if (ga.n < 1 || ga.n > kMaxParents) return hipErrorInvalidValue;
   const int T = ga.a[0].T;
-  if (T < 1 || T > 16) return hipErrorInvalidValue;
+  if (T < 1 || T > 64) return hipErrorInvalidValue;
   if (T <= 4) return run_grouped<1, 4>(ga, stream);
   TileGroup m[kMaxParents];
   for (int p = 0; p < ga.n; ++p) m[p] = TileGroup{ga.a[p].rows / 16, ga.bits[p]};
-  const int rt = tiles_per_workgroup(m, ga.n, 3, 2);
-  if (T <= 8) {
-    if (rt == 1) return run_grouped<1, 8>(ga, stream);
-    return rt == 2 ? run_grouped<2, 8>(ga, stream) : run_grouped<3, 8>(ga, stream);
+  if (T <= 16) {
+    const int rt = tiles_per_workgroup(m, ga.n, 3, 2);
+    if (T <= 8) {
+      if (rt == 1) return run_grouped<1, 8>(ga, stream);
+      return rt == 2 ? run_grouped<2, 8>(ga, stream) : run_grouped<3, 8>(ga, stream);
+    }
+    if (rt == 1) return run_grouped<1, 16>(ga, stream);
+    return rt == 2 ? run_grouped<2, 16>(ga, stream) : run_grouped<3, 16>(ga, stream);
   }
-  if (rt == 1) return run_grouped<1, 16>(ga, stream);
-  return rt == 2 ? run_grouped<2, 16>(ga, stream) : run_grouped<3, 16>(ga, stream);
+  if (T <= 32) {
+    const int rt = tiles_per_workgroup(m, ga.n, 3, 6);
+    if (rt == 1) return run_grouped<1, 32>(ga, stream);
+    return rt == 2 ? run_grouped<2, 32>(ga, stream) : run_grouped<3, 32>(ga, stream);
+  }
+  const int rt = tiles_per_workgroup(m, ga.n, 2, 6);
+  return rt == 1 ? run_grouped<1, 64>(ga, stream) : run_grouped<2, 64>(ga, stream);
 }
 #endif
 

@@ -18,9 +18,9 @@
 //    in a wave-private LDS region, so activation reads never wait behind code loads in the
 //    in-order load counter and no barrier is needed inside the loop: 4 rows through registers
 //    for T <= 4; for K <= 5120, 8 or 16 rows straight from memory (direct-to-LDS loads, no
-//    registers), with 2 or 3 row tiles per workgroup since the slice then allows only one or
-//    two workgroups per compute unit; otherwise the 16-token activation fragments ride in the
-//    same ring as the codes;
+//    registers), with 1 to 3 row tiles per workgroup chosen for an even spread over the compute
+//    units, since the slice then allows only one or two workgroups per compute unit; otherwise
+//    the 16-token activation fragments ride in the same ring as the codes;
 //  * for 17-64 tokens (K <= 5120) a whole slice no longer fits: each wave keeps a ring of
 //    32-row (two slots) or 64-row (one slot) activation tiles, refilled from memory as blocks
 //    are consumed, and feeds every dequantised weight fragment to 2 or 4 16-token steps; the

@@ -16,11 +16,12 @@
 //    non-temporal (each byte is read once per call);
 //  * the wave's activation slice (the token rows of its k-blocks) is loaded first and parked
 //    in a wave-private LDS region, so activation reads never wait behind code loads in the
-//    in-order load counter and no barrier is needed inside the loop: 4 rows through registers
-//    for T <= 4; for K <= 5120, 8 or 16 rows straight from memory (direct-to-LDS loads, no
-//    registers), with 1 to 3 row tiles per workgroup chosen for an even spread over the compute
-//    units, since the slice then allows only one or two workgroups per compute unit; otherwise
-//    the 16-token activation fragments ride in the same ring as the codes;
+//    in-order load counter and no barrier is needed inside the loop: for K <= 5120, 4, 8 or 16
+//    rows straight from memory (direct-to-LDS loads, no registers), the 8- and 16-row ones with
+//    1 to 3 row tiles per workgroup chosen for an even spread over the compute units, since
+//    the slice then allows only one or two workgroups per compute unit; for longer K, 4 rows
+//    through registers (T <= 4), or the 16-token activation fragments ride in the same ring as
+//    the codes;
 //  * for 17-64 tokens (K <= 5120) a whole slice no longer fits: each wave keeps a ring of
 //    32-row (two slots) or 64-row (one slot) activation tiles, refilled from memory as blocks
 //    are consumed, and feeds every dequantised weight fragment to 2 or 4 16-token steps; the
@@ -130,11 +131,22 @@ struct Ring {
   u32x4 xb[XL ? 1 : KPW][4];
 };
 
+// Whether the activation slice goes straight from memory to LDS (direct-to-LDS loads, 16-byte
+// chunks XOR-swizzled by token row): always for 8 and 16 rows, and for 4 rows when a wave's
+// blocks form one chunk of at most five (K <= 5120).  Longer K keeps the 4-row slice in padded
+// rows loaded through registers, chunk by chunk.  (Decode 12288 x 5120, T = 1 / 2 / 4: 8.55 /
+// 8.61 / 9.16 us direct, 8.71 / 8.90 / 9.48 through registers.)
+template <int XL, int KPW, bool LOOP>
+constexpr bool slice_dma() {
+  return XL == 8 || XL == 16 || (XL == 4 && KPW <= 5 && !LOOP);
+}
+
 // XL: token rows of the activation slice held in LDS (0: fragments in the ring instead; 4, 8
 // or 16; 32: a two-block ring of 32-row activation tiles, refilled as the blocks are consumed,
 // and two 16-token matrix-core steps per weight fragment; 64: one 64-row tile slot, refilled
 // with the next block's tile as soon as the current one has been read, and four steps).
-// xdim: XL = 4, fp16 elements per slice row (padded); XL = 8 / 16, k-blocks of the slice.
+// xdim: the slice's k-blocks (direct-to-LDS slices), or fp16 elements per padded row (4 rows
+// through registers).
 // HB: K is not a multiple of 128, so the last k-block holds one group only (without it the
 // per-block test for that case, and its branches, compile away).
 // bx: the workgroup's index among those of this matrix (its row tiles are bx RT ..).
@@ -152,23 +164,25 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
   const int T = a.T;
   const int tr = min(r, T - 1);
   const uint32_t magic = vgpr_const(0x64006400u);
-  // Wave-private activation slice.  4 rows: row t holds the chunk's blocks back to back, rows
-  // xdim elements apart (16 bytes of padding: the rows a fragment read touches hit distinct
-  // banks).  8 / 16 rows: XL x 256 B per k-block, block after block, 16-byte chunk j of row t
-  // stored at chunk j ^ t (no padding: at K = 5120 two 8-row or one 16-row workgroup slice
-  // fill the LDS exactly).
+  // Wave-private activation slice.  Direct-to-LDS (4, 8 or 16 rows): XL x 256 B per k-block,
+  // block after block, 16-byte chunk j of row t stored at chunk j ^ t (no padding: at K = 5120
+  // two 8-row or one 16-row workgroup slice fill the LDS exactly).  4 rows through registers:
+  // row t holds the chunk's blocks back to back, rows xdim elements apart (16 bytes of padding:
+  // the rows a fragment read touches hit distinct banks).
   // 32 / 64 rows: two / one slots of XL rows x 256 B (block i in slot i % 2 / slot 0), chunk j
   // of row t at j ^ (t % 16).
   constexpr bool RING = XL >= 32;
+  constexpr bool XDMA = slice_dma<XL, KPW, LOOP>();  // direct-to-LDS slice
+  constexpr bool XREG = XL == 4 && !XDMA;            // 4-row slice through registers
   constexpr int TH = RING ? XL / 16 : 1;  // 16-token groups per weight fragment
   constexpr int NSLOT = XL == 32 ? 2 : 1;
   constexpr int XBLK = XL * 256;
-  char* const xs = smem + (size_t)wave * (RING ? NSLOT * XBLK : XL >= 8 ? xdim * XBLK : XL * xdim * 2);
+  char* const xs = smem + (size_t)wave * (RING ? NSLOT * XBLK : XDMA ? xdim * XBLK : XL * xdim * 2);
   // 16-byte chunk c (0..15) of token row t of local block i
   auto xchunk = [&](int i, int t, int c) -> const char* {
     if constexpr (RING)
       return xs + (i % NSLOT) * XBLK + t * 256 + ((c ^ (t & 15)) << 4);
-    else if constexpr (XL >= 8)
+    else if constexpr (XDMA)
       return xs + i * XBLK + t * 256 + ((c ^ t) << 4);
     else
       return xs + (t * xdim + i * 128 + c * 8) * 2;
@@ -194,13 +208,13 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
   for (int cb = 0; LOOP ? cb < nbw : (cb == 0 && cb < nbw); cb += KPW) {
     const int nb = min(KPW, nbw - cb);
 
-    // activation slice of this chunk, loaded before any code of the chunk.  4 rows: T <= 4 rows
-    // of nb k-blocks through registers.  8 / 16 rows: one direct-to-LDS instruction per 4 token
-    // rows of a block (lane L: row 4h + L/16, stored chunk L%16 = source chunk (L%16) ^ row);
-    // rows at or beyond T lie past the end of the range-checked buffer and read as zero.
+    // activation slice of this chunk, loaded before any code of the chunk.  Direct-to-LDS: one
+    // instruction per 4 token rows of a block (lane L: row 4h + L/16, stored chunk L%16 =
+    // source chunk (L%16) ^ row); rows at or beyond T lie past the end of the range-checked
+    // buffer and read as zero.  Through registers: T <= 4 rows of nb k-blocks.
     constexpr int XCH = (KPW * 16 + 63) / 64;  // 16-byte chunks per lane per token row
-    u32x4 xr[XL == 4 ? 4 : 1][XL == 4 ? XCH : 1];
-    if constexpr (XL == 4) {
+    u32x4 xr[XREG ? 4 : 1][XREG ? XCH : 1];
+    if constexpr (XREG) {
       const int cpt = nb * 16;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -213,8 +227,8 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
           }
         }
       }
-    } else if constexpr (XL == 8 || XL == 16) {
-      static_assert(!LOOP, "8- and 16-row slices hold one chunk");
+    } else if constexpr (XDMA) {
+      static_assert(!LOOP, "direct-to-LDS slices hold one chunk");
 #pragma unroll
       for (int ib = 0; ib < KPW; ++ib) {
         // (KPW == nb here: the launcher picks the chunk size equal to the wave's block count)
@@ -282,7 +296,7 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
 #pragma unroll
     for (int i = 0; i < D; ++i) issue(i);
 
-    if constexpr (XL == 4) {
+    if constexpr (XREG) {
       const int cpt = nb * 16;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -297,7 +311,7 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    } else if constexpr (XL == 8 || XL == 16) {
+    } else if constexpr (XDMA) {
       // the slice has landed once at most the ring prologue's loads are outstanding
       wait_vmcnt<D * RT * (BITS == 5 ? 4 : 3)>();
     }
@@ -613,11 +627,11 @@ constexpr int ring_depth() {
 
 // Dynamic LDS of one workgroup: the activation slice or ring (nbc blocks per chunk; xdim as
 // passed to the kernel), or the final reduction of the NW partial sums if that is larger.
-template <int MODE, int RT, int XL>
+template <int MODE, int RT, int XL, bool DMA>
 size_t stream_lds(int nbc, int xdim) {
   const size_t x = XL == 32 ? (size_t)kNW * 2 * 32 * 256
                  : XL == 64 ? (size_t)kNW * 64 * 256
-                 : XL >= 8 ? (size_t)kNW * nbc * XL * 256 : XL == 4 ? (size_t)kNW * 4 * xdim * 2 : 0;
+                 : DMA ? (size_t)kNW * nbc * XL * 256 : XL == 4 ? (size_t)kNW * 4 * xdim * 2 : 0;
   const size_t red = MODE == MODE_MFMA ? (size_t)kNW * RT * (XL >= 32 ? XL / 16 : 1) * 64 * 16
                                        : (size_t)kNW * RT * 64 * 4;
   return red > x ? red : x;
@@ -628,8 +642,9 @@ hipError_t run_k(const KArgs& a, hipStream_t stream) {
   const int ntiles = a.rows / 16;
   const int nbw = (a.KB + kNW - 1) / kNW;
   const int nbc = nbw < KPW ? nbw : KPW;  // blocks per chunk
-  const int xdim = XL >= 8 ? nbc : nbc * 128 + 8;
-  const size_t lds = stream_lds<MODE, RT, XL>(nbc, xdim);
+  constexpr bool DMA = slice_dma<XL, KPW, LOOP>();
+  const int xdim = DMA ? nbc : nbc * 128 + 8;
+  const size_t lds = stream_lds<MODE, RT, XL, DMA>(nbc, xdim);
   constexpr int D = ring_depth<RT, XL, KPW>();
   if (a.K % 128)
     hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, D, XL, EPI, LOOP, true>),
@@ -763,8 +778,9 @@ hipError_t run_grouped_k(const GroupedArgs& ga, hipStream_t stream) {
   const KArgs& a = ga.a[0];
   const int nbw = (a.KB + kNW - 1) / kNW;
   const int nbc = nbw < KPW ? nbw : KPW;
-  const int xdim = XL >= 8 ? nbc : nbc * 128 + 8;
-  const size_t lds = stream_lds<MODE_MFMA, RT, XL>(nbc, xdim);
+  constexpr bool DMA = slice_dma<XL, KPW, false>();
+  const int xdim = DMA ? nbc : nbc * 128 + 8;
+  const size_t lds = stream_lds<MODE_MFMA, RT, XL, DMA>(nbc, xdim);
   constexpr int D = ring_depth<RT, XL, KPW>();
   if (a.K % 128)
     hipLaunchKernelGGL((stream_grouped_kernel<MODE_MFMA, RT, kNW, KPW, D, XL, EPI_STORE, false, true>),

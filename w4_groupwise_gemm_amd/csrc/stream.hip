@@ -174,6 +174,12 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
   constexpr bool RING = XL >= 32;
   constexpr bool XDMA = slice_dma<XL, KPW, LOOP>();  // direct-to-LDS slice
   constexpr bool XREG = XL == 4 && !XDMA;            // 4-row slice through registers
+  // Token row of this lane's B column in a direct-to-LDS slice or ring tile: row r itself (mod
+  // the tile's rows), not the clamped T - 1.  Rows at or beyond T hold zeros (the loads past the
+  // end of X read zero) and feed output columns that are never stored; keeping the 16 rows of a
+  // read distinct keeps it free of bank conflicts under the XOR swizzle (with the clamp, T = 4
+  // and T = 8 cost about 80 conflict cycles per wave).
+  const int tl = XDMA || RING ? (r & (XL - 1)) : tr;
   constexpr int TH = RING ? XL / 16 : 1;  // 16-token groups per weight fragment
   constexpr int NSLOT = XL == 32 ? 2 : 1;
   constexpr int XBLK = XL * 256;
@@ -348,12 +354,12 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
             if constexpr (XL > 0)
-              Bf[J] = *reinterpret_cast<const f16x8*>(xchunk(i, tr, 8 * (J >> 1) + 2 * g + (J & 1)));
+              Bf[J] = *reinterpret_cast<const f16x8*>(xchunk(i, tl, 8 * (J >> 1) + 2 * g + (J & 1)));
             else
               Bf[J] = __builtin_bit_cast(f16x8, R.xb[i][J]);
 #pragma unroll
             for (int q = 0; q + 1 < TH; ++q)
-              Bx[q][J] = *reinterpret_cast<const f16x8*>(xchunk(i, min(16 * (q + 1) + r, T - 1), 8 * (J >> 1) + 2 * g + (J & 1)));
+              Bx[q][J] = *reinterpret_cast<const f16x8*>(xchunk(i, (16 * (q + 1) + r) & (XL - 1), 8 * (J >> 1) + 2 * g + (J & 1)));
           }
         }
         if constexpr (XL == 64) {

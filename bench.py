@@ -57,6 +57,8 @@ WORKLOADS = {
     # is not representative of the weight stream
     "tiny": ("tiny", (1,), "linear"),
 }
+ALL_ORDER = ("decode", "tiny", "batched", "swiglu", "prefill")
+METRIC = "W4 GEMM effective weight GB/s (T<=64) and MFMA TFLOP/s (T>=1024), % roofline"
 
 
 # Sources each measured kernel is built from (its own file, the headers it includes and the
@@ -98,7 +100,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="all", choices=["all"] + sorted(WORKLOADS),
+                    help="one configuration, or all of them in one run (decode is the headline)")
     ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of rotated weight copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--route", type=int, default=-1, help="force one route (bench of a schedule)")
@@ -135,14 +138,49 @@ def main() -> int:
 
     import torch
     import w4_groupwise_gemm_amd as w4
-    from synth import make_workload
 
     if args.probe:
         return run_probe(args)
 
-    cfg_name, widths, opname = WORKLOADS[args.workload]
+    if args.workload != "all":
+        line = run_workload(args, args.workload, torch, w4, cpu_timing=not args.no_cpu_baseline)
+        if isinstance(line, int):  # route sweep
+            return line
+        print(json.dumps(line))
+        return 1 if line["parity_ok"] is False else 0
+
+    # Every configuration in one run: decode (the headline, at T = 1, 2, 4) first, then the others,
+    # each with its own cold copies (freed before the next), parity sample and roofline.  The
+    # oracle's timing runs once, on the decode step.
+    if args.widths or args.route >= 0 or args.route_sweep:
+        print("--widths, --route and --route-sweep take one --workload", file=sys.stderr)
+        return 2
+    lines = {}
+    for name in ALL_ORDER:
+        lines[name] = run_workload(args, name, torch, w4,
+                                   cpu_timing=(name == "decode" and not args.no_cpu_baseline))
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    line = dict(lines["decode"])
+    line["per_config"] = {n: {k: v for k, v in l.items() if k not in
+                              ("n_gpus", "steps", "warmup", "higher_is_better", "scaling", "vs_baseline",
+                               "data", "cpu_baseline")}
+                          for n, l in lines.items()}
+    oks = [l["parity_ok"] for l in lines.values()]
+    line["parity_ok"] = None if any(v is None for v in oks) else all(oks)
+    line["metric"] = METRIC
+    print(json.dumps(line))
+    return 1 if line["parity_ok"] is False else 0
+
+
+def run_workload(args, wname, torch, w4, cpu_timing):
+    """Time one workload (all its widths) and check its outputs; returns the JSON record (or the
+    exit status of a route sweep)."""
+    from synth import make_workload
+
+    cfg_name, widths, opname = WORKLOADS[wname]
     all_widths = widths
-    if args.widths:
+    if args.widths and args.workload != "all":
         widths = tuple(int(v) for v in args.widths.split(","))
         # X is drawn once at the largest width (so a token's row is the same at every width)
         all_widths = tuple(sorted(set(all_widths) | set(widths)))
@@ -194,6 +232,7 @@ def main() -> int:
     if args.route_sweep:
         return route_sweep(args, w4, torch, widths, op, pws, xs, res, outs, copies, wstream_alg,
                            N, K, rows, bits)
+    print(f"[bench] {wname}: timing T in {list(widths)}", file=sys.stderr, flush=True)
 
     # ---- outputs of the first launch at each width, kept for the parity check of the
     # cpu_baseline leg (sampled output columns against the fp64 oracle, same run)
@@ -289,7 +328,7 @@ def main() -> int:
         achieved, peak, unit, bound = pd["TFLOPs"], MFMA_F16_PEAK_TFLOPS, "TFLOP/s", "mfma"
     else:
         achieved, peak, unit, bound = pd["alg_GBs"], HBM_PEAK_GBS, "GB/s", "hbm"
-    traffic = traffic_from_profiles(args.workload, dom)
+    traffic = traffic_from_profiles(wname, dom)
     roofline = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
                 "frac": achieved / peak, "traffic": traffic,
                 "kernel": f"T={dom} {pd['route']}", "alg_bytes_per_launch": pd["alg_bytes"],
@@ -311,15 +350,16 @@ def main() -> int:
     if not args.no_cpu_baseline:
         cpu, parity = cpu_baseline(wl, widths, op, bits, lo if not pair else None,
                                    hi if not pair else None, sc if not pair else None,
-                                   ze if not pair else None, wstream_alg, prefill, rows, K, gpu_out)
-        print(f"[bench] parity {parity}", file=sys.stderr, flush=True)
+                                   ze if not pair else None, wstream_alg, prefill, rows, K, gpu_out,
+                                   timing=cpu_timing)
+        print(f"[bench] {wname} parity {parity}", file=sys.stderr, flush=True)
     parity_ok = None if parity is None else all(p["ok"] for p in parity.values())
 
     line = {
         "metric": metric, "value": value, "unit": unit_v, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {'SwiGLU pair ' if pair else ''}W{bits} N={N} "
+        "config": {"workload": f"{wname}: {'SwiGLU pair ' if pair else ''}W{bits} N={N} "
                                f"K={K} group=64, T in {list(widths)}, cold ({copies} copies)",
                    "N": N, "K": K, "bits": bits, "T": list(widths), "op": opname,
                    "cold_copies": copies, "parallelism": "none (1 GPU)"},
@@ -328,8 +368,9 @@ def main() -> int:
     }
     if context:
         line["context"] = context
-    print(json.dumps(line))
-    return 1 if parity_ok is False else 0
+    del pws
+    return line
+
 
 
 def context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, dev):
@@ -632,7 +673,8 @@ def traffic_summary(args) -> int:
     return 0
 
 
-def cpu_baseline(wl, widths, op, bits, lo, hi, sc, ze, wstream_alg, prefill, rows, K, gpu_out):
+def cpu_baseline(wl, widths, op, bits, lo, hi, sc, ze, wstream_alg, prefill, rows, K, gpu_out,
+                 timing=True):
     """The fp64 oracle on the host cores: (1) the parity check of this run's GPU outputs on 256
     sampled output columns per width; (2) the oracle timed on a bounded sample of the same step.
     Returns (baseline record, parity record)."""
@@ -651,7 +693,10 @@ def cpu_baseline(wl, widths, op, bits, lo, hi, sc, ze, wstream_alg, prefill, row
                 ref = ref + wl.r[:T][:, cols].astype(np.float64)
         rel = oracle.rel_l2(got, ref)
         elem = float(np.max(np.abs(got - ref) / (1.0 + np.abs(ref))))
-        parity[str(T)] = {"rel_l2": rel, "max_elem": elem, "ok": bool(rel <= 2e-3 and elem <= 1e-2)}
+        parity[str(T)] = {"rel_l2": rel, "max_elem": elem, "ok": bool(rel <= 2e-3 and elem <= 1e-2),
+                          "sampled_columns": int(len(cols))}
+    if not timing:
+        return None, parity
     try:
         import threadpoolctl
         threads = max(p["num_threads"] for p in threadpoolctl.threadpool_info()) or 1

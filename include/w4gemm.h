@@ -22,7 +22,8 @@
  *     argument synchronously first, then enqueue exactly one kernel on `stream` and return
  *     without synchronising: they are asynchronous and may be captured into a HIP graph.
  *   - On any error the call returns a negative w4_status before touching device memory;
- *     `out` is left untouched.
+ *     `out` is left untouched.  W4_ERR_LAUNCH is the status of this call's own kernel launch
+ *     (hipLaunchKernel's return value), not an error left pending by earlier work.
  *   - The library is stateless apart from a per-device "is gfx950" cache, so concurrent calls
  *     on different streams are safe.
  */
@@ -87,10 +88,12 @@ typedef enum {
  *   packed row tile 2i+1 = up rows 16i..16i+15, i.e. a packed matrix of 2N rows.
  * ---------------------------------------------------------------------------------------- */
 
-/* Bytes of the packed code buffer for an N x K matrix; 0 if the shape is invalid. */
+/* Bytes of the packed code buffer for an N x K matrix; 0 if the shape is invalid.  (Sizes of
+ * this library's own packed layout: no passage of the pages defines them.) */
 size_t w4_packed_bytes(int N, int K, int bits, int group);
 
-/* Bytes of EACH of the packed scales and zeros buffers; 0 if the shape is invalid. */
+/* Bytes of EACH of the packed scales and zeros buffers; 0 if the shape is invalid.  (Likewise
+ * library-defined.) */
 size_t w4_packed_sz_bytes(int N, int K, int group);
 
 /* Repack one matrix from the canonical format (host memory in, host memory out).
@@ -171,6 +174,9 @@ const char* w4_route_name(int route_id); /* NULL for an unknown id */
 /* T domain [*tmin, *tmax] of a route; W4_ERR_DOMAIN for an unknown id. */
 int w4_route_domain(int route_id, int* tmin, int* tmax);
 
+/* Library plumbing; no passage of the pages defines these two.  w4_status_str: a static,
+ * NUL-terminated description of a w4_status (never NULL; "unknown status" for other values).
+ * w4_layout_version: W4_LAYOUT_VERSION of the packed layout this library reads and writes. */
 const char* w4_status_str(int status);
 int w4_layout_version(void);
 

@@ -11,10 +11,10 @@ Sources (the pages this library is built from):
   plane plus a high-bit plane; the k order inside a group is free.
 * ninfer-3080 performance notes, section "A8 prefill routes" (route table):
   LinearAdd, a projection whose result is added to a residual.
-* ARK research, "Fused kernels", section "Why standard kernels stall": the fused
-  kernel unpacks the weights and multiplies them in one pass; the result is the
-  plain unpack-then-multiply product, which is what this oracle computes in
-  two separate, unfused steps.
+* ARK research, "Fused kernels", section "Why standard kernels stall": a fused
+  low-bit kernel returns the ordinary product of the activations with the
+  dequantised weights; this oracle forms that product in two separate steps
+  (dequantise everything, then multiply).
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): the dequantised weight is ``w = s * (q - z)`` with the zero-point

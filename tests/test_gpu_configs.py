@@ -74,3 +74,29 @@ def test_config_full_size(name, T):
         if wl.op == "add":
             ref = ref + wl.r[:T][:, cols].astype(np.float64)
     assert_close(got, ref, f"{name} T={T}")
+
+
+FULL_CASES = [("decode", 1), ("decode", 4), ("batched", 64), ("swiglu", 16), ("prefill", 1024)]
+
+
+@pytest.mark.parametrize("name,T", FULL_CASES, ids=[f"{n}-T{t}" for n, t in FULL_CASES])
+def test_config_every_output(name, T):
+    """The same configurations checked over every output element (the oracle over all N)."""
+    wl, pw, canon, bits = _prepared(name)
+    op = {"swiglu": w4.OP_SWIGLU, "add": w4.OP_ADD}.get(wl.op, w4.OP_LINEAR)
+    route = w4.route_name(w4.route_for(op, bits, T, pw.N, pw.K))
+    print(f"case config-all config={name} T={T} N={pw.N} K={pw.K} bits={bits} route={route}", flush=True)
+    x = wl.x[:T]
+    xd = torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    if wl.op == "swiglu":
+        y = w4.linear_swiglu(xd, pw)
+        ref = oracle.swiglu(x, canon[0], canon[1], bits=bits)
+    elif wl.op == "add":
+        r = np.ascontiguousarray(wl.r[:T])
+        y = w4.linear_add(xd, pw, torch.from_numpy(r).to(DEV))
+        ref = oracle.linear_add(x, *canon, r, bits=bits)
+    else:
+        y = w4.linear(xd, pw)
+        ref = oracle.linear(x, *canon, bits=bits)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().numpy().astype(np.float64), ref, f"{name} T={T} all outputs")

@@ -182,7 +182,7 @@ def test_long_k(route, K):
     """K ranges that take the 8-, 16-block and looping variants of the streaming kernels,
     including a half-empty last k-block (12352 = 96.5 blocks)."""
     N = 48
-    for op in (w4.OP_LINEAR, w4.OP_ADD):
+    for op in (w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD):
         for bits in (4, 5):
             for T in (ROUTE_TS[route][0], ROUTE_TS[route][-1]):
                 ws, x, r = _case(N, K, T, bits, op, seed=K + T + bits + op, outliers=2)
@@ -192,3 +192,22 @@ def test_long_k(route, K):
                 print(f"case long-k route={route} op={op} bits={bits} T={T} K={K}", flush=True)
                 y = w4.linear_route(route_ids()[route], op, xd, pw, residual=rd)
                 assert_close(to_np(y), _oracle(ws, x, r, op, bits), f"{route} K{K} op{op} b{bits} T{T}")
+
+
+@pytest.mark.parametrize("route", ["gemv_exact_t", "mfma_stream_t16"])
+@pytest.mark.parametrize("K", [640, 6144])
+def test_two_tile_workgroups_many_rows(route, K):
+    """At T <= 4 matrices of 32768 rows or more take the streaming kernel's two-row-tile
+    workgroups (4-row activation slice), for K up to 5120 (one chunk) and beyond (chunk loop);
+    checked against the oracle on 512 sampled output columns, including the first and last."""
+    N, bits = 32768, 4
+    rng = np.random.default_rng(K + 3)
+    ws = make_weights(rng, "w", N, K, bits, ("uniform", 6, 9), (0.005, 0.02))
+    pw = w4.pack_weight(*canon(ws), bits, device=DEV)
+    x, _ = make_activations(rng, 4, K, 1.0, 3)
+    cols = np.unique(np.concatenate([np.sort(rng.choice(N, 512, replace=False)), [0, 1, N - 1]]))
+    for T in (1, 2, 3, 4):
+        print(f"case two-tile route={route} T={T} N={N} K={K}", flush=True)
+        y = w4.linear_route(route_ids()[route], w4.OP_LINEAR, torch.from_numpy(x[:T]).to(DEV), pw)
+        got = to_np(y)[:, cols]
+        assert_close(got, oracle.linear_rows(x[:T], *canon(ws), bits, cols), f"{route} T{T} K{K}")

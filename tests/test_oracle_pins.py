@@ -16,7 +16,9 @@ What pins what:
   product unchanged), here with power-of-two factors per group so that it is bit-exact;
 * k-permutation within a group (ninfer-3080 performance notes, "What changed",
   "Permuted k order"), whole-group permutation, row permutation, token independence;
-* silu against scipy's logistic function and textbook values; LinearAdd special cases.
+* silu against scipy's logistic function and textbook values; LinearAdd special cases;
+* the sampled-column form (linear_rows) against exact rational sums on an unsorted,
+  repeated row subset, and against the full product's columns.
 
 ``test_planted_mistakes_are_caught`` plants plausible mistakes in the oracle and
 checks that at least one pin fails for each.
@@ -287,10 +289,40 @@ def check_linear_add():
     assert np.array_equal(out, y + r.astype(np.float64))
 
 
+def check_linear_rows():
+    """linear_rows (the sampled-column oracle of the full-size checks) against the exact
+    rational sum for an unsorted row subset with repeats, and against linear()'s columns."""
+    rng = np.random.default_rng(31)
+    eps = 2.0 ** -53
+    for bits in (4, 5):
+        N, K, T = 7, 128, 2
+        q, lo, hi, s, z, x = _tiny_case(rng, N, K, T, bits)
+        rows = [5, 0, 5, 3, 6, 1]
+        y = ref.linear_rows(x, lo, hi, s, z, bits, rows)
+        assert y.shape == (T, len(rows))
+        for j, n in enumerate(rows):
+            codes = _bitstring_codes(lo[n], None if hi is None else hi[n], K, bits)
+            for t in range(T):
+                exact = Fraction(0)
+                mag = Fraction(0)
+                for k in range(K):
+                    g = k // 64
+                    term = Fraction(float(x[t, k])) * Fraction(float(s[n, g])) * (
+                        codes[k] - Fraction(float(z[n, g])))
+                    exact += term
+                    mag += abs(term)
+                err = abs(Fraction(float(y[t, j])) - exact)
+                assert err <= (K + 4) * eps * mag, (bits, n, t, float(err))
+        full = ref.linear(x, lo, hi, s, z, bits)
+        sub = full[:, rows]
+        assert np.max(np.abs(y - sub)) <= 1e-14 * max(1.0, float(np.max(np.abs(sub))))
+
+
 ALL_CHECKS = [
     check_unpack_fixtures, check_hand_dequant, check_bruteforce_exact,
     check_integer_special_case, check_closed_forms, check_equalisation_power_of_two,
     check_equalisation_general, check_permutations, check_silu_and_swiglu, check_linear_add,
+    check_linear_rows,
 ]
 
 
@@ -378,9 +410,25 @@ def _mut_transposed_rows(x, lo, hi, scales, zeros, bits, group=64, n_chunk=2048)
     return y[:, ::-1].copy()
 
 
+def _mut_rows_sorted(x, lo, hi, scales, zeros, bits, rows, group=64):
+    # the subset taken in sorted order without repeats
+    return _orig_linear_rows(x, lo, hi, scales, zeros, bits, sorted(set(int(r) for r in rows)), group)
+
+
+def _mut_rows_scales_unselected(x, lo, hi, scales, zeros, bits, rows, group=64):
+    # codes of the selected rows, but scales and zeros of the first len(rows) rows
+    rows = np.asarray(rows, dtype=np.int64)
+    K = np.asarray(x).shape[1]
+    q = ref.unpack_codes(lo[rows], None if hi is None else hi[rows], K, bits)
+    n = len(rows)
+    w = ref.dequantize(q, scales[:n], zeros[:n], group)
+    return np.asarray(x).astype(np.float64) @ w.T
+
+
 _orig_unpack = ref.unpack_codes
 _orig_dequant = ref.dequantize
 _orig_linear = ref.linear
+_orig_linear_rows = ref.linear_rows
 
 MUTATIONS = {
     "nibble_order": ("unpack_codes", _mut_nibble_order),
@@ -392,6 +440,8 @@ MUTATIONS = {
     "silu_sign": ("silu", _mut_silu_sign),
     "dropped_residual": ("linear_add", _mut_no_residual),
     "reversed_rows": ("linear", _mut_transposed_rows),
+    "subset_rows_sorted": ("linear_rows", _mut_rows_sorted),
+    "subset_scales_unselected": ("linear_rows", _mut_rows_scales_unselected),
 }
 
 

@@ -216,26 +216,62 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _check_tensor(t, name: str, shape, dtype, device) -> None:
+    """Raise ValueError unless t is a contiguous tensor of `dtype` and `shape` on `device`.
+
+    The library receives bare pointers, so everything it cannot check (the device a pointer
+    belongs to, the element type, the extent) is checked here, before any launch."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def _check_x(x, K: int):
     import torch
-    if x.dtype != torch.float16 or not x.is_cuda or x.dim() != 2 or x.shape[1] != K:
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise ValueError("x must be a CUDA tensor of shape [T, K]")
+    if x.dim() != 2:
         raise ValueError("x must be a CUDA float16 tensor of shape [T, K]")
-    if not x.is_contiguous():
-        raise ValueError("x must be contiguous")
+    _check_tensor(x, "x", (x.shape[0], K), torch.float16, x.device)
+
+
+def _check_weight(pw: "PackedWeight", device) -> None:
+    """The packed tensors must live on the activations' device and hold what the shape needs."""
+    import torch
+    rows = 2 * pw.N if pw.pair else pw.N
+    nw, nsz = packed_bytes(rows, pw.K, pw.bits), packed_sz_bytes(rows, pw.K)
+    _check_tensor(pw.w, "packed codes", (nw,), torch.uint8, device)
+    _check_tensor(pw.scales, "packed scales", (nsz // 2,), torch.int16, device)
+    _check_tensor(pw.zeros, "packed zero-points", (nsz // 2,), torch.int16, device)
+
+
+def _check_residual(residual, T: int, N: int, like) -> None:
+    import torch
+    _check_tensor(residual, "residual", (T, N), torch.float16, like.device)
 
 
 def _out(out, T: int, N: int, like):
     import torch
     if out is None:
         return torch.empty((T, N), dtype=torch.float16, device=like.device)
-    if out.dtype != torch.float16 or out.shape != (T, N) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float16 tensor of shape [T, N]")
+    _check_tensor(out, "out", (T, N), torch.float16, like.device)
     return out
 
 
 def linear(x, pw: PackedWeight, out=None, stream=None):
     """out[T, N] = x . dequant(W)^T (fp16) via ``w4_linear``."""
+    if pw.pair:
+        raise ValueError("a gate/up pair runs through linear_swiglu")
     _check_x(x, pw.K)
+    _check_weight(pw, x.device)
     T = x.shape[0]
     out = _out(out, T, pw.N, x)
     _check(lib().w4_linear(_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros), T, pw.N,
@@ -248,6 +284,7 @@ def linear_swiglu(x, pw: PackedWeight, out=None, stream=None):
     if not pw.pair:
         raise ValueError("linear_swiglu needs a gate/up pair from pack_pair")
     _check_x(x, pw.K)
+    _check_weight(pw, x.device)
     T = x.shape[0]
     out = _out(out, T, pw.N, x)
     _check(lib().w4_linear_swiglu(_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros), T,
@@ -258,8 +295,12 @@ def linear_swiglu(x, pw: PackedWeight, out=None, stream=None):
 
 def linear_add(x, pw: PackedWeight, residual, out=None, stream=None):
     """out[T, N] = x . dequant(W)^T + residual via ``w4_linear_add`` (out may be residual)."""
+    if pw.pair:
+        raise ValueError("a gate/up pair runs through linear_swiglu")
     _check_x(x, pw.K)
+    _check_weight(pw, x.device)
     T = x.shape[0]
+    _check_residual(residual, T, pw.N, x)
     out = _out(out, T, pw.N, x)
     _check(lib().w4_linear_add(_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros),
                                _dptr(residual), T, pw.N, pw.K, pw.bits, GROUP, _dptr(out),
@@ -275,8 +316,12 @@ def linear_grouped(x, pws, outs=None, stream=None):
         raise ValueError("linear_grouped takes 1 to 4 single matrices with one K")
     K = pws[0].K
     _check_x(x, K)
+    for pw in pws:
+        _check_weight(pw, x.device)
     T = x.shape[0]
     outs = [None] * len(pws) if outs is None else list(outs)
+    if len(outs) != len(pws):
+        raise ValueError("one output per matrix")
     outs = [_out(o, T, pw.N, x) for o, pw in zip(outs, pws)]
     arr = (_Parent * len(pws))(*[_Parent(_dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros), pw.N, pw.bits,
                                          _dptr(o)) for pw, o in zip(pws, outs)])
@@ -289,7 +334,16 @@ def linear_route(route_id: int, op: int, x, pw: PackedWeight, residual=None, out
                  stream=None):
     """Run one specific route (benches and per-route parity tests)."""
     _check_x(x, pw.K)
+    _check_weight(pw, x.device)
+    if op == OP_SWIGLU and not pw.pair:
+        raise ValueError("the SwiGLU op needs a gate/up pair from pack_pair")
+    if op != OP_SWIGLU and pw.pair:
+        raise ValueError("a gate/up pair runs the SwiGLU op only")
     T = x.shape[0]
+    if op == OP_ADD:
+        _check_residual(residual, T, pw.N, x)
+    else:
+        residual = None
     out = _out(out, T, pw.N, x)
     _check(lib().w4_linear_route(route_id, op, _dptr(x), _dptr(pw.w), _dptr(pw.scales),
                                  _dptr(pw.zeros), _dptr(residual), T, pw.N, pw.K, pw.bits, GROUP,

@@ -1,5 +1,5 @@
-// Device-side building blocks shared by the kernels: vector types, the in-register decode of
-// packed 4/5-bit codes, the fp16 dequantisation, the matrix-core step and the epilogues.
+// Device-side building blocks shared by the kernels: vector types, wait and register helpers,
+// the in-register decode of packed 4/5-bit codes, the matrix-core steps and the epilogues.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -21,21 +21,41 @@ enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ADD = 2 };
 
 __device__ __forceinline__ f16x2 as_h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
 
-// Exact codes q as four fp16 pairs -- slots (0,1), (2,3), (4,5), (6,7) -- of packed dword J.
-// OR-ing a 4-bit field into the mantissa of fp16 1024.0 (0x6400) gives 1024 + q exactly
-// (bits 0..3) or 1024 + 16 q (bits 4..7); one packed add or fma removes the bias.  For 5-bit
-// codes bit 4 is OR-ed in from the lane's high-plane word at mantissa bit 4 (resp. 8), which
-// the high-plane bit positions of the packed layout make one shift + one mask-or per pair.
-// This is the "magic-bias" decode the ninfer-3080 performance notes mention ("What changed",
-// "Permuted k order"), done here with fp16 instead of bf16 and without integer-to-float ops.
+// A 32-bit register that holds the constant (keeps v_and_or_b32 legal: one literal or SGPR).
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// (a & mask) | c in one v_and_or_b32 (the compiler can otherwise form and + and + or3)
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(c));
+  return r;
+}
+
+// Biased fp16 pairs of packed dword J: 1024 + q (slots 0,1 and 4,5) and 1024 + 16 q (slots 2,3
+// and 6,7).  OR-ing a 4-bit field into the mantissa of fp16 1024.0 (magic = 0x64006400) gives
+// 1024 + q exactly, with no integer-to-float conversion (the "magic-bias" decode of the
+// ninfer-3080 performance notes, "What changed", "Permuted k order", here in fp16).  For 5-bit
+// codes bit 4 comes from the lane's high-plane word at mantissa bit 4 (resp. 8), one shift and
+// one mask-or per pair given the packed high-plane bit positions.
 template <int BITS, int J>
-__device__ __forceinline__ void decode_q(uint32_t w, uint32_t hiw, f16x2 q[4]) {
-  constexpr uint32_t kMagic = 0x64006400u;  // fp16 1024.0 in both halves
+__device__ __forceinline__ void wbiased(uint32_t w, uint32_t hiw, uint32_t magic, uint32_t u[4]) {
   const uint32_t w8 = w >> 8;
-  uint32_t u0 = (w & 0x000F000Fu) | kMagic;   // 1024 + q      (slots 0, 1)
-  uint32_t u1 = (w & 0x00F000F0u) | kMagic;   // 1024 + 16 q   (slots 2, 3)
-  uint32_t u2 = (w8 & 0x000F000Fu) | kMagic;  // 1024 + q      (slots 4, 5)
-  uint32_t u3 = (w8 & 0x00F000F0u) | kMagic;  // 1024 + 16 q   (slots 6, 7)
+  u[0] = and_or(w, 0x000F000Fu, magic);
+  u[1] = and_or(w, 0x00F000F0u, magic);
+  u[2] = and_or(w8, 0x000F000Fu, magic);
+  u[3] = and_or(w8, 0x00F000F0u, magic);
   if constexpr (BITS == 5) {
     constexpr int t = (J == 0 ? 0 : J == 1 ? 2 : J == 2 ? 8 : 10);
     uint32_t x1, x2;
@@ -46,33 +66,17 @@ __device__ __forceinline__ void decode_q(uint32_t w, uint32_t hiw, f16x2 q[4]) {
       x1 = hiw >> (t - 4);
       x2 = hiw >> (t - 3);
     }
-    u0 |= x1 & 0x00100010u;
-    u1 |= x1 & 0x01000100u;
-    u2 |= x2 & 0x00100010u;
-    u3 |= x2 & 0x01000100u;
+    u[0] = and_or(x1, 0x00100010u, u[0]);
+    u[1] = and_or(x1, 0x01000100u, u[1]);
+    u[2] = and_or(x2, 0x00100010u, u[2]);
+    u[3] = and_or(x2, 0x01000100u, u[3]);
   }
-  const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f};
-  const f16x2 c64 = {(f16)64.0f, (f16)64.0f};
-  const f16x2 c16th = {(f16)0.0625f, (f16)0.0625f};
-  q[0] = as_h2(u0) - c1024;
-  q[1] = as_h2(u1) * c16th - c64;
-  q[2] = as_h2(u2) - c1024;
-  q[3] = as_h2(u3) * c16th - c64;
 }
 
 __device__ __forceinline__ f16x8 cat8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
   const f16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
   const f16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
   return __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// fp16 weights w = (q - z) * s for the 8 slots of packed dword J (one rounding when z is an
-// integer: q - z is then exact in fp16).  z2 / s2 hold the group's zero-point / scale twice.
-template <int BITS, int J>
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, uint32_t hiw, f16x2 z2, f16x2 s2) {
-  f16x2 q[4];
-  decode_q<BITS, J>(w, hiw, q);
-  return cat8((q[0] - z2) * s2, (q[1] - z2) * s2, (q[2] - z2) * s2, (q[3] - z2) * s2);
 }
 
 // Broadcast the fp16 value in the low (H == 0) or high (H == 1) half of a packed pair.

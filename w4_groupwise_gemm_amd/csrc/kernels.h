@@ -6,6 +6,21 @@
 
 namespace w4 {
 
+template <typename T>
+struct same_type {
+  using type = T;
+};
+
+// Enqueue one kernel on `stream` and return the status of this launch itself (hipLaunchKernel's
+// return value), so that an error left behind by unrelated earlier work is not reported as
+// this call's failure.  The arguments are converted to the kernel's parameter types.
+template <typename... P>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds,
+                                hipStream_t stream, typename same_type<P>::type... args) {
+  void* argv[sizeof...(P) + 1] = {static_cast<void*>(&args)..., nullptr};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, stream);
+}
+
 struct KArgs {
   const _Float16* x;     // [T][K] activations
   const uint8_t* w;      // packed codes, `rows` packed rows

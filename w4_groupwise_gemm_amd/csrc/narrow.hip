@@ -415,9 +415,8 @@ hipError_t run(const KArgs& a, hipStream_t stream) {
   const size_t lds = rings > red ? rings : red;
   const int ntb = (a.T + BN - 1) / BN;
   if (ntb > 65535) return hipErrorInvalidConfiguration;  // grid y limit (T above 4 million)
-  hipLaunchKernelGGL((narrow_kernel<BITS, NP, NTT, NC, DC, DX, EPI>), dim3(grid, ntb),
-                     dim3(64 * (NC + 2)), lds, stream, a);
-  return hipGetLastError();
+  return launch_kernel(&narrow_kernel<BITS, NP, NTT, NC, DC, DX, EPI>, dim3(grid, ntb),
+                       dim3(64 * (NC + 2)), lds, stream, a);
 }
 
 template <int BITS, int NTT, int EPI>

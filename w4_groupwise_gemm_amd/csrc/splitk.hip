@@ -188,9 +188,8 @@ hipError_t run_k(const KArgs& a, hipStream_t stream) {
   const int grid = (npairs + NP - 1) / NP;
   const size_t lds = (size_t)kNW * NP * 16 * 64 * 4;
   constexpr int D = (NP == 1 && !LOOP) ? 3 : 2;  // blocks in flight per wave (register budget)
-  hipLaunchKernelGGL((splitk_kernel<BITS, NP, kNW, KPW, D, EPI, LOOP>), dim3(grid), dim3(kNW * 64), lds,
-                     stream, a);
-  return hipGetLastError();
+  return launch_kernel(&splitk_kernel<BITS, NP, kNW, KPW, D, EPI, LOOP>, dim3(grid), dim3(kNW * 64), lds,
+                       stream, a);
 }
 
 template <int BITS, int NP, int EPI>

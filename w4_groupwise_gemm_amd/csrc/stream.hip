@@ -48,45 +48,13 @@ using w4layout::block_bytes;
 
 enum { MODE_MFMA = 0, MODE_DOT2 = 1 };
 
-// A 32-bit register that holds the constant (keeps v_and_or_b32 legal: one literal/SGPR).
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-  return r;
-}
-
-// Biased fp16 pairs 1024 + q (slots 0,1 / 4,5) and 1024 + 16 q (slots 2,3 / 6,7) of dword J.
-template <int BITS, int J>
-__device__ __forceinline__ void biased_pairs(uint32_t w, uint32_t hiw, uint32_t magic, uint32_t u[4]) {
-  const uint32_t w8 = w >> 8;
-  u[0] = (w & 0x000F000Fu) | magic;
-  u[1] = (w & 0x00F000F0u) | magic;
-  u[2] = (w8 & 0x000F000Fu) | magic;
-  u[3] = (w8 & 0x00F000F0u) | magic;
-  if constexpr (BITS == 5) {
-    constexpr int t = (J == 0 ? 0 : J == 1 ? 2 : J == 2 ? 8 : 10);
-    uint32_t x1, x2;
-    if constexpr (t <= 3) {
-      x1 = hiw << (4 - t);
-      x2 = hiw << (3 - t);
-    } else {
-      x1 = hiw >> (t - 4);
-      x2 = hiw >> (t - 3);
-    }
-    u[0] |= x1 & 0x00100010u;
-    u[1] |= x1 & 0x01000100u;
-    u[2] |= x2 & 0x00100010u;
-    u[3] |= x2 & 0x01000100u;
-  }
-}
-
 // fp16 weights (q - z) * s of dword J as four pairs.  FAST: z is an integer (1024 + z and
 // 64 + z exact in fp16), b0 = -(1024 + z), b1 = -(64 + z).  Otherwise q is made exact first.
 template <int BITS, int J, bool FAST>
 __device__ __forceinline__ void weights(uint32_t w, uint32_t hiw, uint32_t magic, f16x2 z2, f16x2 b0,
                                         f16x2 b1, f16x2 s2, f16x2 out[4]) {
   uint32_t u[4];
-  biased_pairs<BITS, J>(w, hiw, magic, u);
+  wbiased<BITS, J>(w, hiw, magic, u);
   const f16x2 c16th = {(f16)0.0625f, (f16)0.0625f};
   if constexpr (FAST) {
     out[0] = (as_h2(u[0]) + b0) * s2;
@@ -100,14 +68,6 @@ __device__ __forceinline__ void weights(uint32_t w, uint32_t hiw, uint32_t magic
     out[2] = ((as_h2(u[2]) - c1024) - z2) * s2;
     out[3] = ((as_h2(u[3]) * c16th - c64) - z2) * s2;
   }
-}
-
-// Wait until at most n vector-memory operations of this wave are outstanding (vmcnt in bits
-// 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // The same for an n that is a constant once the caller's loop is unrolled.
@@ -652,13 +612,12 @@ hipError_t run_k(const KArgs& a, hipStream_t stream) {
   const int xdim = DMA ? nbc : nbc * 128 + 8;
   const size_t lds = stream_lds<MODE, RT, XL, DMA>(nbc, xdim);
   constexpr int D = ring_depth<RT, XL, KPW>();
+  const dim3 grid((ntiles + RT - 1) / RT), block(kNW * 64);
   if (a.K % 128)
-    hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, D, XL, EPI, LOOP, true>),
-                       dim3((ntiles + RT - 1) / RT), dim3(kNW * 64), lds, stream, a, xdim);
-  else
-    hipLaunchKernelGGL((stream_kernel<BITS, MODE, RT, kNW, KPW, D, XL, EPI, LOOP, false>),
-                       dim3((ntiles + RT - 1) / RT), dim3(kNW * 64), lds, stream, a, xdim);
-  return hipGetLastError();
+    return launch_kernel(&stream_kernel<BITS, MODE, RT, kNW, KPW, D, XL, EPI, LOOP, true>, grid, block,
+                         lds, stream, a, xdim);
+  return launch_kernel(&stream_kernel<BITS, MODE, RT, kNW, KPW, D, XL, EPI, LOOP, false>, grid, block,
+                       lds, stream, a, xdim);
 }
 
 // k-blocks per wave: one unrolled chunk for K <= 16384 (exactly the wave's block count up to
@@ -789,12 +748,10 @@ hipError_t run_grouped_k(const GroupedArgs& ga, hipStream_t stream) {
   const size_t lds = stream_lds<MODE_MFMA, RT, XL, DMA>(nbc, xdim);
   constexpr int D = ring_depth<RT, XL, KPW>();
   if (a.K % 128)
-    hipLaunchKernelGGL((stream_grouped_kernel<MODE_MFMA, RT, kNW, KPW, D, XL, EPI_STORE, false, true>),
+    return launch_kernel(&stream_grouped_kernel<MODE_MFMA, RT, kNW, KPW, D, XL, EPI_STORE, false, true>,
+                         dim3(total), dim3(kNW * 64), lds, stream, g, xdim);
+  return launch_kernel(&stream_grouped_kernel<MODE_MFMA, RT, kNW, KPW, D, XL, EPI_STORE, false, false>,
                        dim3(total), dim3(kNW * 64), lds, stream, g, xdim);
-  else
-    hipLaunchKernelGGL((stream_grouped_kernel<MODE_MFMA, RT, kNW, KPW, D, XL, EPI_STORE, false, false>),
-                       dim3(total), dim3(kNW * 64), lds, stream, g, xdim);
-  return hipGetLastError();
 }
 
 template <int RT, int XL>

@@ -13,52 +13,6 @@ using w4layout::block_bytes;
 
 constexpr int kXCD = 8;  // gfx950 (MI350 series): 8 accelerator complex dies, round-robin dispatch
 
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
-  return r;
-}
-
-// Wait until at most n vector-memory operations of this wave are outstanding (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// (a & mask) | c in one v_and_or_b32 (the compiler otherwise forms and + and + or3)
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(c));
-  return r;
-}
-
-// Biased fp16 pairs 1024 + q (slots 0,1 / 4,5) and 1024 + 16 q (slots 2,3 / 6,7) of dword J.
-template <int BITS, int J>
-__device__ __forceinline__ void wbiased(uint32_t w, uint32_t hiw, uint32_t magic, uint32_t u[4]) {
-  const uint32_t w8 = w >> 8;
-  u[0] = and_or(w, 0x000F000Fu, magic);
-  u[1] = and_or(w, 0x00F000F0u, magic);
-  u[2] = and_or(w8, 0x000F000Fu, magic);
-  u[3] = and_or(w8, 0x00F000F0u, magic);
-  if constexpr (BITS == 5) {
-    constexpr int t = (J == 0 ? 0 : J == 1 ? 2 : J == 2 ? 8 : 10);
-    uint32_t x1, x2;
-    if constexpr (t <= 3) {
-      x1 = hiw << (4 - t);
-      x2 = hiw << (3 - t);
-    } else {
-      x1 = hiw >> (t - 4);
-      x2 = hiw >> (t - 3);
-    }
-    u[0] = and_or(x1, 0x00100010u, u[0]);
-    u[1] = and_or(x1, 0x01000100u, u[1]);
-    u[2] = and_or(x2, 0x00100010u, u[2]);
-    u[3] = and_or(x2, 0x01000100u, u[3]);
-  }
-}
-
 // fp16 weights (q - z) * s of packed dword J (8 k slots of one row).  FAST: z is an integer,
 // so 1024 + z and 64 + z are exact and one packed add (or fma) removes bias and zero-point.
 template <int BITS, int J, bool FAST>

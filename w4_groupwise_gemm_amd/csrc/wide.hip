@@ -327,9 +327,8 @@ hipError_t run(const KArgs& a, hipStream_t stream) {
   const int nrb = (ntiles + TILES - 1) / TILES;
   const int ntb = (a.T + BN - 1) / BN;
   const size_t lds = (size_t)2 * BN * 256;
-  hipLaunchKernelGGL((wide_kernel<BITS, NP, NTT, EPI, OCC>), dim3(nrb * ntb), dim3(256), lds,
-                     stream, a, nrb, ntb);
-  return hipGetLastError();
+  return launch_kernel(&wide_kernel<BITS, NP, NTT, EPI, OCC>, dim3(nrb * ntb), dim3(256), lds,
+                       stream, a, nrb, ntb);
 }
 
 template <int BITS, int EPI>

@@ -3,7 +3,7 @@
  * for AMD Instinct MI355X (gfx950).
  *
  *   Y[T, N] = X[T, K] . dequant(Wq)[N, K]^T,   dequant(Wq)[n, k] = s[n, g] * (q[n, k] - z[n, g]),
- *   g = k / 64,  q in [0, 2^bits),  bits in {4, 5}.
+ *   g = k / group,  q in [0, 2^bits),  bits in {4, 5},  group in {32, 64, 128} (64 measured).
  *
  * Sources.  The operation is the fused kernel of ARK research "Fused kernels" (section "Why
  * standard kernels stall": unpack the low-bit weights and multiply in one pass shaped for a
@@ -19,8 +19,9 @@
  *   - Device pointers are owned by the caller; the library never allocates, frees or keeps
  *     them.  Host pointers (repack) are likewise the caller's.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Compute calls validate every
- *     argument synchronously first, then enqueue exactly one kernel on `stream` and return
- *     without synchronising: they are asynchronous and may be captured into a HIP graph.
+ *     argument synchronously first, then enqueue exactly one kernel on `stream` (the bf16 calls:
+ *     two) and return without synchronising: they are asynchronous and may be captured into a
+ *     HIP graph.
  *   - On any error the call returns a negative w4_status before touching device memory;
  *     `out` is left untouched.  W4_ERR_LAUNCH is the status of this call's own kernel launch
  *     (hipLaunchKernel's return value), not an error left pending by earlier work.
@@ -41,8 +42,9 @@ extern "C" {
 
 typedef enum {
   W4_OK = 0,
-  W4_ERR_INVALID_ARG = -1, /* null pointer, negative or zero size, N % 16 or K % 64 not 0   */
-  W4_ERR_UNSUPPORTED = -2, /* bits not in {4,5}, group != 64, unknown op                    */
+  W4_ERR_INVALID_ARG = -1, /* null pointer, negative or zero size, N % 16 or K % 64 not 0
+                              (K % 128 for groups of 128), workspace too small              */
+  W4_ERR_UNSUPPORTED = -2, /* bits not in {4,5}, group not in {32,64,128}, unknown op       */
   W4_ERR_MISALIGNED = -3,  /* a pointer is not 16-byte aligned                              */
   W4_ERR_ALIAS = -4,       /* out overlaps an input (out == residual exactly is allowed)    */
   W4_ERR_DOMAIN = -5,      /* route forced outside its T domain, or route id unknown        */
@@ -61,7 +63,8 @@ typedef enum {
  *   5-bit: lo as above holds bits 0..3; hi uint8 [N][K/8] holds bit 4:
  *          (hi[n][k/8] >> (k&7)) & 1  (the 4-bit plane + high-bit plane of the ninfer-3080
  *          performance notes, "What changed", Q5 bullet).
- *   scales, zeros: fp16 [N][K/64].
+ *   scales, zeros: fp16 [N][K/group].  The pages use one scale per 64 columns (ninfer-3080
+ *   performance notes, "cuBLAS prefill route"); groups of 32 and 128 are variants.
  *
  * Packed (device) layout -- what the compute calls read.  Row tiles of 16 rows, k-blocks of
  * 128 columns, KB = ceil(K/128).  Byte image of one (row tile rt, k-block kb) block:
@@ -77,10 +80,15 @@ typedef enum {
  *   (ninfer-3080 performance notes, "What changed", "Permuted k order").
  *   5-bit high plane: the lane's 32-bit word holds bit 4 of slot e of dword j at bit
  *       t_j + r_e,  t = {0, 2, 8, 10},  r = {0, 16, 4, 20, 1, 17, 5, 21}.
- *   scales / zeros: fp16 [N/16][KB][16][2]; element (rt, kb, r, h) = value of row 16*rt + r,
- *   group 2*kb + h.
- *   When K % 128 == 64 the second group of the last k-block is padding: codes 0, scale 0,
- *   zero 0.  Repacking is a bit-exact permutation plus that zero padding.
+ *   scales / zeros, group 64: fp16 [N/16][KB][16][2]; element (rt, kb, r, h) = value of row
+ *   16*rt + r, group 2*kb + h (the group of the lane's dwords 2h, 2h+1).
+ *   group 32: fp16 [N/16][KB][2][16][2]; element (rt, kb, p, r, h) = group 4*kb + 2*h + p of
+ *   row 16*rt + r (the group of dwords 2h, 2h+1 of lane groups g = 2p, 2p+1).
+ *   group 128: as group 64 with both halves of a pair equal to group kb (the kernels read every
+ *   group size as pairs; this costs N*K/64 bytes of scales and zeros, twice the minimum).
+ *   When K % 128 == 64 the second half of the last k-block is padding: codes 0, and its scale
+ *   and zero entries 0.  Repacking is a bit-exact permutation plus that zero padding (and, for
+ *   groups of 128, the duplicated pair halves).
  *   The packed form of a row-concatenation [A; B] (same K, bits) is the byte concatenation of
  *   the packed forms of A and B, so parents that share one activation can be packed into one
  *   buffer and run as one call.
@@ -133,6 +141,33 @@ int w4_linear_add(const uint16_t* x, const void* w, const uint16_t* scales, cons
                   const uint16_t* residual, int T, int N, int K, int bits, int group,
                   uint16_t* out, void* stream);
 
+/* ---- bf16 activations.  The same three ops with x, out (and residual) in bf16; weights,
+ * scales and zero-points are the packed fp16 format above.  Each token row t is first copied to
+ * the workspace as fp16 X[t] * 2^-e_t, with the power of two e_t (also stored in the workspace)
+ * chosen from the row's largest magnitude so that the copy is exact for every value down to
+ * 2^-17 of that magnitude; the kernel then runs the fp16 path and its epilogue scales the fp32
+ * sums by 2^e_t, applies SwiGLU or adds the bf16 residual in fp32, and rounds once to bf16.
+ * The pages' kernels run their activations in bf16 (ninfer-3080 performance notes, "What
+ * changed", "Permuted k order").  Two kernels are enqueued per call (the copy, then the route
+ * the fp16 op would take at the same T).  workspace: caller-owned device memory of at least
+ * w4_bf16_workspace_bytes(T, K) bytes, 16-byte aligned, overlapping no argument; its contents
+ * are scratch between calls.  Validation and errors as the fp16 calls, plus W4_ERR_INVALID_ARG
+ * for a missing or short workspace and W4_ERR_ALIAS for an overlapping one. */
+size_t w4_bf16_workspace_bytes(int T, int K); /* 0 if the shape is invalid */
+
+int w4_linear_bf16(const uint16_t* x, const void* w, const uint16_t* scales, const uint16_t* zeros,
+                   int T, int N, int K, int bits, int group, uint16_t* out, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+int w4_linear_swiglu_bf16(const uint16_t* x, const void* w_pair, const uint16_t* scales_pair,
+                          const uint16_t* zeros_pair, int T, int N, int K, int bits, int group,
+                          uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
+int w4_linear_add_bf16(const uint16_t* x, const void* w, const uint16_t* scales,
+                       const uint16_t* zeros, const uint16_t* residual, int T, int N, int K,
+                       int bits, int group, uint16_t* out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* ---- grouped call: several matrices that share one activation (ninfer-3080 performance notes,
  * "What changed": two parents over one activation; the projections that read one activation
  * with 4-bit and 5-bit weights).  One matrix of the group, as w4_repack output: */
@@ -168,6 +203,13 @@ int w4_route_for(int op, int bits, int T, int N, int K);
 int w4_linear_route(int route_id, int op, const uint16_t* x, const void* w,
                     const uint16_t* scales, const uint16_t* zeros, const uint16_t* residual,
                     int T, int N, int K, int bits, int group, uint16_t* out, void* stream);
+
+/* Run a specific route with bf16 activations (as w4_linear_route, with the workspace of the
+ * bf16 calls above). */
+int w4_linear_route_bf16(int route_id, int op, const uint16_t* x, const void* w,
+                         const uint16_t* scales, const uint16_t* zeros, const uint16_t* residual,
+                         int T, int N, int K, int bits, int group, uint16_t* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
 
 int w4_route_count(void);
 const char* w4_route_name(int route_id); /* NULL for an unknown id */

@@ -20,5 +20,6 @@ from .reference import (  # noqa: F401
     swiglu,
     linear_add,
     fp16_round,
+    bf16_value,
     rel_l2,
 )

@@ -139,6 +139,17 @@ def linear_add(x, lo, hi, scales, zeros, r, bits: int, group: int = GROUP) -> np
     return linear(x, lo, hi, scales, zeros, bits, group) + np.asarray(r).astype(np.float64)
 
 
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> their exact values in fp64.
+
+    A bfloat16 number is the upper 16 bits of an IEEE binary32 number (sign, 8 exponent bits,
+    7 mantissa bits), so its value is that of the binary32 word ``bits << 16``.  Used for the
+    bf16-activation calls, whose inputs and outputs are bf16 (the pages' kernels run their
+    activations in bf16: ninfer-3080 performance notes, "What changed")."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
 def fp16_round(y: np.ndarray) -> np.ndarray:
     """Round fp64 values to fp16 with round-to-nearest-even (numpy's cast)."""
     return np.asarray(y, dtype=np.float64).astype(np.float16)

@@ -13,4 +13,6 @@ from .inputs import (  # noqa: F401
     make_residual,
     make_workload,
     pack_canonical,
+    bf16_bits,
+    make_activations_bf16,
 )

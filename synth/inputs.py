@@ -105,11 +105,12 @@ def pack_canonical(q: np.ndarray, bits: int) -> Tuple[np.ndarray, Optional[np.nd
 
 
 def make_weights(rng: np.random.Generator, name: str, N: int, K: int, bits: int,
-                 zero: Sequence, scale: Tuple[float, float]) -> WeightSet:
-    """Draw codes, then zeros, then scales (in that order) for one matrix."""
-    if K % GROUP:
-        raise ValueError("K must be a multiple of 64")
-    G = K // GROUP
+                 zero: Sequence, scale: Tuple[float, float], group: int = GROUP) -> WeightSet:
+    """Draw codes, then zeros, then scales (in that order) for one matrix; one scale and one
+    zero-point per `group` columns (64 in every measured configuration)."""
+    if K % max(group, 64):
+        raise ValueError("K must be a multiple of 64 (of 128 for groups of 128)")
+    G = K // group
     q = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
     if zero[0] == "const":
         zeros = np.full((N, G), zero[1], dtype=np.float16)
@@ -143,6 +144,26 @@ def make_activations(rng: np.random.Generator, T: int, K: int, sigma: float,
 
 def make_residual(rng: np.random.Generator, T: int, N: int) -> np.ndarray:
     return rng.standard_normal((T, N)).astype(np.float16)
+
+
+def bf16_bits(x) -> np.ndarray:
+    """float32 values -> bfloat16 bit patterns (uint16), rounded to nearest even: the input
+    format of the bf16 calls (numpy has no bfloat16 type).  Finite inputs only."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
+
+
+def make_activations_bf16(rng: np.random.Generator, T: int, K: int, sigma: float,
+                          n_outliers: int, factor: float = OUTLIER_FACTOR
+                          ) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """As make_activations, rounded to bf16 instead of fp16: uint16 bit patterns [T, K]."""
+    x = (rng.standard_normal((T, K)) * sigma).astype(np.float32)
+    idx = None
+    if n_outliers:
+        idx = np.sort(rng.choice(K, n_outliers, replace=False))
+        x[:, idx] *= np.float32(factor)
+    return bf16_bits(x), idx
 
 
 def make_workload(name: str, seed: int = 0, Ts: Optional[Sequence[int]] = None) -> Workload:

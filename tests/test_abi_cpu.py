@@ -79,8 +79,12 @@ def _call(fn, x=0x10000, w=0x20000000, s=0x30000000, z=0x40000000, T=4, N=256, K
 def test_validation_errors(fn):
     assert _call(fn, bits=3) == -2
     assert _call(fn, bits=8) == -2
-    assert _call(fn, group=32) == -2
-    assert _call(fn, group=128) == -2
+    assert _call(fn, group=16) == -2
+    assert _call(fn, group=48) == -2
+    assert _call(fn, group=128, K=320) == -1   # groups of 128 need K % 128 == 0
+    # groups of 32 and 128 pass validation (no GPU here: the device check is what fails)
+    assert _call(fn, group=32) == -6
+    assert _call(fn, group=128) == -6
     assert _call(fn, N=250) == -1
     assert _call(fn, N=0) == -1
     assert _call(fn, K=500) == -1
@@ -132,22 +136,33 @@ def test_packed_sizes():
     assert w4.packed_bytes(256, 500, 4) == 0
     assert w4.packed_bytes(256, 512, 6) == 0
     assert w4.packed_bytes(256, 512, 4) == w4.lib().w4_packed_bytes(256, 512, 4, 64)
-    assert w4.lib().w4_packed_bytes(256, 512, 4, 32) == 0
+    assert w4.lib().w4_packed_bytes(256, 512, 4, 16) == 0
+    # codes do not depend on the group size; scales / zeros: one pair per row and 128 columns,
+    # two for groups of 32
+    assert w4.packed_bytes(256, 512, 4, 32) == w4.packed_bytes(256, 512, 4, 128) == 256 * 512 // 2
+    assert w4.packed_sz_bytes(256, 512, 32) == 2 * w4.packed_sz_bytes(256, 512, 64)
+    assert w4.packed_sz_bytes(256, 512, 128) == w4.packed_sz_bytes(256, 512, 64)
+    assert w4.packed_sz_bytes(256, 320, 128) == 0
+    assert w4.bf16_workspace_bytes(3, 512) == 3 * 512 * 2 + 16
+    assert w4.bf16_workspace_bytes(1, 100) == 0
 
 
 # ---- repacking: C++ vs the independent layout model, and round trips
 
+@pytest.mark.parametrize("group", [64, 32, 128])
 @pytest.mark.parametrize("bits", [4, 5])
 @pytest.mark.parametrize("N,K", [(16, 64), (16, 128), (32, 192), (48, 512), (16, 320)])
-def test_repack_matches_spec(bits, N, K):
-    rng = np.random.default_rng(N * 1000 + K + bits)
-    ws = make_weights(rng, "w", N, K, bits, ("real", 0, 1 << bits), (0.001, 0.05))
-    w, s, z = w4.repack(ws.lo, ws.hi, ws.scales, ws.zeros, bits)
-    w2, s2, z2 = spec_pack(ws.q.astype(np.int64), ws.scales, ws.zeros, bits)
+def test_repack_matches_spec(bits, N, K, group):
+    if K % max(64, group):
+        pytest.skip("groups of 128 need K % 128 == 0")
+    rng = np.random.default_rng(N * 1000 + K + bits + group)
+    ws = make_weights(rng, "w", N, K, bits, ("real", 0, 1 << bits), (0.001, 0.05), group=group)
+    w, s, z = w4.repack(ws.lo, ws.hi, ws.scales, ws.zeros, bits, group)
+    w2, s2, z2 = spec_pack(ws.q.astype(np.int64), ws.scales, ws.zeros, bits, group)
     assert np.array_equal(w, w2)
     assert np.array_equal(s, s2)
     assert np.array_equal(z, z2)
-    q, su, zu = spec_unpack(w, s, z, N, K, bits)
+    q, su, zu = spec_unpack(w, s, z, N, K, bits, group)
     assert np.array_equal(q, ws.q.astype(np.int64))
     assert np.array_equal(su, ws.scales.view(np.uint16))
     assert np.array_equal(zu, ws.zeros.view(np.uint16))
@@ -213,7 +228,8 @@ def test_repack_is_deterministic_and_validates():
     assert L.w4_repack(ptr, None, ptr, ptr, 16, 64, 5, 64, ptr, ptr, ptr) == -1
     assert L.w4_repack(ptr, ptr, ptr, ptr, 16, 64, 4, 64, ptr, ptr, ptr) == -1
     assert L.w4_repack(ptr, None, ptr, ptr, 16, 64, 6, 64, ptr, ptr, ptr) == -2
-    assert L.w4_repack(ptr, None, ptr, ptr, 16, 64, 4, 32, ptr, ptr, ptr) == -2
+    assert L.w4_repack(ptr, None, ptr, ptr, 16, 64, 4, 16, ptr, ptr, ptr) == -2
+    assert L.w4_repack(ptr, None, ptr, ptr, 16, 64, 4, 128, ptr, ptr, ptr) == -1  # K % 128
     assert L.w4_repack(ptr, None, ptr, ptr, 15, 64, 4, 64, ptr, ptr, ptr) == -1
     assert L.w4_repack(None, None, ptr, ptr, 16, 64, 4, 64, ptr, ptr, ptr) == -1
 
@@ -235,9 +251,38 @@ def test_grouped_validation():
     assert _grouped([a, b[:4] + (3,) + b[5:]]) == -2                      # 3-bit codes
     assert _grouped([a, b[:3] + (250,) + b[4:]]) == -1                    # N % 16
     assert _grouped([a, b], K=500) == -1                                  # K % 64
-    assert _grouped([a, b], group=128) == -2
+    assert _grouped([a, b], group=48) == -2
+    assert _grouped([a, b], group=32) == -6
     assert _grouped([a, b[:5] + (0x51000002,)]) == -3                     # misaligned output
     assert _grouped([a, b[:5] + (0x50000000 + 64,)]) == -4                # outputs overlap
     assert _grouped([a, b[:5] + (0x20000000 + 64,)]) == -4                # output over another's codes
     assert _grouped([a, b[:5] + (0x10000 + 16,)]) == -4                   # output over x
     assert _grouped([a, b], T=0) == 0                                     # T == 0: no-op
+
+
+# ---- bf16 calls: validation of the workspace on top of the fp16 rules (fake addresses)
+
+def _call_bf16(fn, ws=0x70000000, ws_bytes=None, T=4, N=256, K=512, group=64, x=0x10000,
+               out=0x50000000):
+    L = w4.lib()
+    nb = w4.bf16_workspace_bytes(T, K) if ws_bytes is None else ws_bytes
+    w, s, z, res = 0x20000000, 0x30000000, 0x40000000, 0x60000000
+    if fn == "add":
+        return L.w4_linear_add_bf16(x, w, s, z, res, T, N, K, 4, group, out, ws, nb, None)
+    if fn == "swiglu":
+        return L.w4_linear_swiglu_bf16(x, w, s, z, T, N, K, 4, group, out, ws, nb, None)
+    return L.w4_linear_bf16(x, w, s, z, T, N, K, 4, group, out, ws, nb, None)
+
+
+@pytest.mark.parametrize("fn", ["linear", "swiglu", "add"])
+def test_bf16_validation(fn):
+    assert _call_bf16(fn) == -6                       # valid: stops at the device check
+    assert _call_bf16(fn, group=32) == -6
+    assert _call_bf16(fn, ws=0) == -1                 # no workspace
+    assert _call_bf16(fn, ws_bytes=100) == -1         # short workspace
+    assert _call_bf16(fn, ws=0x70000008) == -3        # misaligned
+    assert _call_bf16(fn, ws=0x10000 + 16) == -4      # over x
+    assert _call_bf16(fn, ws=0x50000000 - 16) == -4   # over out
+    assert _call_bf16(fn, ws=0x30000000) == -4        # over the scales
+    assert _call_bf16(fn, T=0, ws=0, x=0, out=0) == 0  # T == 0 is a no-op
+    assert _call_bf16(fn, group=16) == -2

@@ -318,11 +318,41 @@ def check_linear_rows():
         assert np.max(np.abs(y - sub)) <= 1e-14 * max(1.0, float(np.max(np.abs(sub))))
 
 
+def check_group_sizes():
+    """Groups of 32 and 128 columns (variants of the pages' 64): exact rational sums with the
+    group index k // group, for an unsorted mix of scales and integer or fractional zeros."""
+    rng = np.random.default_rng(41)
+    eps = 2.0 ** -53
+    for group in (32, 128):
+        for bits in (4, 5):
+            N, K, T = 3, 256, 2
+            q = rng.integers(0, 1 << bits, size=(N, K), dtype=np.uint8)
+            G = K // group
+            s = rng.uniform(0.005, 0.02, size=(N, G)).astype(np.float16)
+            z = rng.uniform(0, 1 << bits, size=(N, G)).astype(np.float16)
+            x = rng.standard_normal((T, K)).astype(np.float16)
+            lo, hi = pack_canonical(q, bits)
+            y = ref.linear(x, lo, hi, s, z, bits, group=group)
+            for n in range(N):
+                codes = _bitstring_codes(lo[n], None if hi is None else hi[n], K, bits)
+                for t in range(T):
+                    exact = Fraction(0)
+                    mag = Fraction(0)
+                    for k in range(K):
+                        g = k // group
+                        term = Fraction(float(x[t, k])) * Fraction(float(s[n, g])) * (
+                            codes[k] - Fraction(float(z[n, g])))
+                        exact += term
+                        mag += abs(term)
+                    err = abs(Fraction(float(y[t, n])) - exact)
+                    assert err <= (K + 4) * eps * mag, (group, bits, n, t, float(err))
+
+
 ALL_CHECKS = [
     check_unpack_fixtures, check_hand_dequant, check_bruteforce_exact,
     check_integer_special_case, check_closed_forms, check_equalisation_power_of_two,
     check_equalisation_general, check_permutations, check_silu_and_swiglu, check_linear_add,
-    check_linear_rows,
+    check_linear_rows, check_group_sizes,
 ]
 
 
@@ -342,6 +372,31 @@ def test_generator_packs_fixtures():
             assert hi2 is None
         else:
             assert np.array_equal(hi2, hi)
+
+
+def test_bf16_value_fixed_points():
+    """bf16 bit patterns against values fixed by the format (sign, 8 exponent bits, 7 mantissa
+    bits): powers of two, the largest finite value, the smallest subnormal, a decimal."""
+    bits = np.array([0x3F80, 0xC000, 0x3DCD, 0x0001, 0x7F7F, 0x8000, 0x4049, 0x0080], dtype=np.uint16)
+    want = [1.0, -2.0, 0.10009765625, 2.0 ** -133, (2 - 2.0 ** -7) * 2.0 ** 127, -0.0,
+            3.140625, 2.0 ** -126]
+    got = oracle.bf16_value(bits)
+    for g, w, b in zip(got, want, bits):
+        assert g == w and np.signbit(g) == np.signbit(w), (hex(int(b)), g, w)
+    assert np.isinf(oracle.bf16_value(np.array([0x7F80], np.uint16))[0])
+    assert np.isnan(oracle.bf16_value(np.array([0x7FC0], np.uint16))[0])
+
+
+def test_generator_bf16_rounding():
+    """The bf16 input generator rounds to nearest, ties to even."""
+    from synth import bf16_bits
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -20, -2.5, 0.1],
+                 dtype=np.float32)
+    got = bf16_bits(x)
+    assert list(got) == [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020, 0x3DCD], [hex(int(v)) for v in got]
+    # every bf16 value survives the round trip exactly
+    allb = np.arange(0, 0x7F80, 7, dtype=np.uint16)
+    assert np.array_equal(bf16_bits(oracle.bf16_value(allb).astype(np.float32)), allb)
 
 
 def test_rel_l2_and_round():
@@ -410,6 +465,14 @@ def _mut_transposed_rows(x, lo, hi, scales, zeros, bits, group=64, n_chunk=2048)
     return y[:, ::-1].copy()
 
 
+def _mut_group_fixed(q, scales, zeros, group=64):
+    # the group size ignored: column k takes entry k // 64 of the scale and zero arrays
+    s = np.asarray(scales, np.float64)
+    z = np.asarray(zeros, np.float64)
+    idx = np.minimum(np.arange(q.shape[1]) // 64, s.shape[1] - 1)
+    return s[:, idx] * (q - z[:, idx])
+
+
 def _mut_rows_sorted(x, lo, hi, scales, zeros, bits, rows, group=64):
     # the subset taken in sorted order without repeats
     return _orig_linear_rows(x, lo, hi, scales, zeros, bits, sorted(set(int(r) for r in rows)), group)
@@ -442,6 +505,7 @@ MUTATIONS = {
     "reversed_rows": ("linear", _mut_transposed_rows),
     "subset_rows_sorted": ("linear_rows", _mut_rows_sorted),
     "subset_scales_unselected": ("linear_rows", _mut_rows_scales_unselected),
+    "group_size_ignored": ("dequantize", _mut_group_fixed),
 }
 
 

@@ -28,10 +28,14 @@ GROUP = 64
 _STATUS = {0: "W4_OK", -1: "W4_ERR_INVALID_ARG", -2: "W4_ERR_UNSUPPORTED", -3: "W4_ERR_MISALIGNED",
            -4: "W4_ERR_ALIAS", -5: "W4_ERR_DOMAIN", -6: "W4_ERR_DEVICE", -7: "W4_ERR_LAUNCH"}
 
+GROUPS = (32, 64, 128)
+
 EXPORTS = (
     "w4_packed_bytes", "w4_packed_sz_bytes", "w4_repack", "w4_repack_pair", "w4_linear",
     "w4_linear_swiglu", "w4_linear_add", "w4_route_for", "w4_linear_route", "w4_route_count",
     "w4_route_name", "w4_route_domain", "w4_status_str", "w4_layout_version", "w4_linear_grouped",
+    "w4_bf16_workspace_bytes", "w4_linear_bf16", "w4_linear_swiglu_bf16", "w4_linear_add_bf16",
+    "w4_linear_route_bf16",
 )
 
 
@@ -90,6 +94,16 @@ def lib() -> ctypes.CDLL:
     L.w4_linear_grouped.argtypes = [vp, ctypes.POINTER(_Parent), i, i, i, i, vp]
     L.w4_linear_grouped.restype = i
     L.w4_layout_version.restype = i
+    L.w4_bf16_workspace_bytes.argtypes = [i, i]
+    L.w4_bf16_workspace_bytes.restype = sz
+    L.w4_linear_bf16.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, sz, vp]
+    L.w4_linear_bf16.restype = i
+    L.w4_linear_swiglu_bf16.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, sz, vp]
+    L.w4_linear_swiglu_bf16.restype = i
+    L.w4_linear_add_bf16.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, sz, vp]
+    L.w4_linear_add_bf16.restype = i
+    L.w4_linear_route_bf16.argtypes = [i, i, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, sz, vp]
+    L.w4_linear_route_bf16.restype = i
     _lib = L
     return L
 
@@ -105,12 +119,16 @@ def _check(status: int, where: str) -> None:
 
 # ------------------------------------------------------------------ host-side repacking
 
-def packed_bytes(N: int, K: int, bits: int) -> int:
-    return int(lib().w4_packed_bytes(N, K, bits, GROUP))
+def packed_bytes(N: int, K: int, bits: int, group: int = GROUP) -> int:
+    return int(lib().w4_packed_bytes(N, K, bits, group))
 
 
-def packed_sz_bytes(N: int, K: int) -> int:
-    return int(lib().w4_packed_sz_bytes(N, K, GROUP))
+def packed_sz_bytes(N: int, K: int, group: int = GROUP) -> int:
+    return int(lib().w4_packed_sz_bytes(N, K, group))
+
+
+def bf16_workspace_bytes(T: int, K: int) -> int:
+    return int(lib().w4_bf16_workspace_bytes(T, K))
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -129,38 +147,38 @@ def _host(a, dtype) -> Optional[np.ndarray]:
     return a
 
 
-def repack(lo, hi, scales, zeros, bits: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+def repack(lo, hi, scales, zeros, bits: int, group: int = GROUP) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """Canonical host arrays -> packed (codes uint8, scales uint16, zeros uint16) host arrays."""
     lo = _host(lo, np.uint8)
     hi = _host(hi, np.uint8)
     s = _host(scales, np.uint16)
     z = _host(zeros, np.uint16)
     N, K = lo.shape[0], lo.shape[1] * 2
-    nw, nsz = packed_bytes(N, K, bits), packed_sz_bytes(N, K)
+    nw, nsz = packed_bytes(N, K, bits, group), packed_sz_bytes(N, K, group)
     if nw == 0 or nsz == 0:
         raise W4Error(-1, "repack")
     w = np.empty(nw, dtype=np.uint8)
     so = np.empty(nsz // 2, dtype=np.uint16)
     zo = np.empty(nsz // 2, dtype=np.uint16)
-    _check(lib().w4_repack(_ptr(lo), _ptr(hi), _ptr(s), _ptr(z), N, K, bits, GROUP,
+    _check(lib().w4_repack(_ptr(lo), _ptr(hi), _ptr(s), _ptr(z), N, K, bits, group,
                            _ptr(w), _ptr(so), _ptr(zo)), "w4_repack")
     return w, so, zo
 
 
-def repack_pair(gate, up, bits: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+def repack_pair(gate, up, bits: int, group: int = GROUP) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """gate/up = (lo, hi, scales, zeros) canonical host tuples -> interleaved pair layout."""
     g = [_host(gate[0], np.uint8), _host(gate[1], np.uint8), _host(gate[2], np.uint16),
          _host(gate[3], np.uint16)]
     u = [_host(up[0], np.uint8), _host(up[1], np.uint8), _host(up[2], np.uint16),
          _host(up[3], np.uint16)]
     N, K = g[0].shape[0], g[0].shape[1] * 2
-    nw, nsz = packed_bytes(2 * N, K, bits), packed_sz_bytes(2 * N, K)
+    nw, nsz = packed_bytes(2 * N, K, bits, group), packed_sz_bytes(2 * N, K, group)
     if nw == 0 or nsz == 0:
         raise W4Error(-1, "repack_pair")
     w = np.empty(nw, dtype=np.uint8)
     so = np.empty(nsz // 2, dtype=np.uint16)
     zo = np.empty(nsz // 2, dtype=np.uint16)
-    _check(lib().w4_repack_pair(*[_ptr(a) for a in g], *[_ptr(a) for a in u], N, K, bits, GROUP,
+    _check(lib().w4_repack_pair(*[_ptr(a) for a in g], *[_ptr(a) for a in u], N, K, bits, group,
                                 _ptr(w), _ptr(so), _ptr(zo)), "w4_repack_pair")
     return w, so, zo
 
@@ -177,6 +195,7 @@ class PackedWeight:
     K: int
     bits: int
     pair: bool = False
+    group: int = GROUP  # columns per scale / zero-point group (32, 64 or 128)
 
     @property
     def nbytes_stream(self) -> int:
@@ -185,24 +204,24 @@ class PackedWeight:
 
 
 def to_device(packed: Tuple[np.ndarray, np.ndarray, np.ndarray], N: int, K: int, bits: int,
-              pair: bool = False, device="cuda") -> PackedWeight:
+              pair: bool = False, device="cuda", group: int = GROUP) -> PackedWeight:
     import torch
     w, s, z = packed
     return PackedWeight(torch.from_numpy(w).to(device),
                         torch.from_numpy(s.view(np.int16)).to(device),
-                        torch.from_numpy(z.view(np.int16)).to(device), N, K, bits, pair)
+                        torch.from_numpy(z.view(np.int16)).to(device), N, K, bits, pair, group)
 
 
-def pack_weight(lo, hi, scales, zeros, bits: int, device="cuda") -> PackedWeight:
+def pack_weight(lo, hi, scales, zeros, bits: int, device="cuda", group: int = GROUP) -> PackedWeight:
     lo = np.asarray(lo)
-    return to_device(repack(lo, hi, scales, zeros, bits), lo.shape[0], lo.shape[1] * 2, bits,
-                     False, device)
+    return to_device(repack(lo, hi, scales, zeros, bits, group), lo.shape[0], lo.shape[1] * 2, bits,
+                     False, device, group)
 
 
-def pack_pair(gate, up, bits: int, device="cuda") -> PackedWeight:
+def pack_pair(gate, up, bits: int, device="cuda", group: int = GROUP) -> PackedWeight:
     lo = np.asarray(gate[0])
-    return to_device(repack_pair(gate, up, bits), lo.shape[0], lo.shape[1] * 2, bits, True,
-                     device)
+    return to_device(repack_pair(gate, up, bits, group), lo.shape[0], lo.shape[1] * 2, bits, True,
+                     device, group)
 
 
 def _dptr(t) -> Optional[int]:
@@ -234,35 +253,36 @@ def _check_tensor(t, name: str, shape, dtype, device) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
-def _check_x(x, K: int):
+def _check_x(x, K: int, dtype=None):
     import torch
+    dtype = torch.float16 if dtype is None else dtype
     if not isinstance(x, torch.Tensor) or not x.is_cuda:
         raise ValueError("x must be a CUDA tensor of shape [T, K]")
     if x.dim() != 2:
-        raise ValueError("x must be a CUDA float16 tensor of shape [T, K]")
-    _check_tensor(x, "x", (x.shape[0], K), torch.float16, x.device)
+        raise ValueError(f"x must be a CUDA {dtype} tensor of shape [T, K]")
+    _check_tensor(x, "x", (x.shape[0], K), dtype, x.device)
 
 
 def _check_weight(pw: "PackedWeight", device) -> None:
     """The packed tensors must live on the activations' device and hold what the shape needs."""
     import torch
     rows = 2 * pw.N if pw.pair else pw.N
-    nw, nsz = packed_bytes(rows, pw.K, pw.bits), packed_sz_bytes(rows, pw.K)
+    nw, nsz = packed_bytes(rows, pw.K, pw.bits, pw.group), packed_sz_bytes(rows, pw.K, pw.group)
     _check_tensor(pw.w, "packed codes", (nw,), torch.uint8, device)
     _check_tensor(pw.scales, "packed scales", (nsz // 2,), torch.int16, device)
     _check_tensor(pw.zeros, "packed zero-points", (nsz // 2,), torch.int16, device)
 
 
 def _check_residual(residual, T: int, N: int, like) -> None:
-    import torch
-    _check_tensor(residual, "residual", (T, N), torch.float16, like.device)
+    # the residual and the output have the activations' dtype (float16 or bfloat16)
+    _check_tensor(residual, "residual", (T, N), like.dtype, like.device)
 
 
 def _out(out, T: int, N: int, like):
     import torch
     if out is None:
-        return torch.empty((T, N), dtype=torch.float16, device=like.device)
-    _check_tensor(out, "out", (T, N), torch.float16, like.device)
+        return torch.empty((T, N), dtype=like.dtype, device=like.device)
+    _check_tensor(out, "out", (T, N), like.dtype, like.device)
     return out
 
 
@@ -275,7 +295,7 @@ def linear(x, pw: PackedWeight, out=None, stream=None):
     T = x.shape[0]
     out = _out(out, T, pw.N, x)
     _check(lib().w4_linear(_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros), T, pw.N,
-                           pw.K, pw.bits, GROUP, _dptr(out), _stream(stream)), "w4_linear")
+                           pw.K, pw.bits, pw.group, _dptr(out), _stream(stream)), "w4_linear")
     return out
 
 
@@ -288,7 +308,7 @@ def linear_swiglu(x, pw: PackedWeight, out=None, stream=None):
     T = x.shape[0]
     out = _out(out, T, pw.N, x)
     _check(lib().w4_linear_swiglu(_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros), T,
-                                  pw.N, pw.K, pw.bits, GROUP, _dptr(out), _stream(stream)),
+                                  pw.N, pw.K, pw.bits, pw.group, _dptr(out), _stream(stream)),
            "w4_linear_swiglu")
     return out
 
@@ -303,7 +323,7 @@ def linear_add(x, pw: PackedWeight, residual, out=None, stream=None):
     _check_residual(residual, T, pw.N, x)
     out = _out(out, T, pw.N, x)
     _check(lib().w4_linear_add(_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros),
-                               _dptr(residual), T, pw.N, pw.K, pw.bits, GROUP, _dptr(out),
+                               _dptr(residual), T, pw.N, pw.K, pw.bits, pw.group, _dptr(out),
                                _stream(stream)), "w4_linear_add")
     return out
 
@@ -312,8 +332,8 @@ def linear_grouped(x, pws, outs=None, stream=None):
     """[x . dequant(W_p)^T for each packed matrix p] via ``w4_linear_grouped`` (1 to 4 matrices,
     4- or 5-bit, same K, not SwiGLU pairs): one launch for T <= 64 and K <= 5120."""
     pws = list(pws)
-    if not 1 <= len(pws) <= 4 or any(pw.pair for pw in pws) or len({pw.K for pw in pws}) != 1:
-        raise ValueError("linear_grouped takes 1 to 4 single matrices with one K")
+    if not 1 <= len(pws) <= 4 or any(pw.pair for pw in pws) or len({(pw.K, pw.group) for pw in pws}) != 1:
+        raise ValueError("linear_grouped takes 1 to 4 single matrices with one K and group size")
     K = pws[0].K
     _check_x(x, K)
     for pw in pws:
@@ -325,7 +345,7 @@ def linear_grouped(x, pws, outs=None, stream=None):
     outs = [_out(o, T, pw.N, x) for o, pw in zip(outs, pws)]
     arr = (_Parent * len(pws))(*[_Parent(_dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros), pw.N, pw.bits,
                                          _dptr(o)) for pw, o in zip(pws, outs)])
-    _check(lib().w4_linear_grouped(_dptr(x), arr, len(pws), T, K, GROUP, _stream(stream)),
+    _check(lib().w4_linear_grouped(_dptr(x), arr, len(pws), T, K, pws[0].group, _stream(stream)),
            "w4_linear_grouped")
     return outs
 
@@ -346,9 +366,76 @@ def linear_route(route_id: int, op: int, x, pw: PackedWeight, residual=None, out
         residual = None
     out = _out(out, T, pw.N, x)
     _check(lib().w4_linear_route(route_id, op, _dptr(x), _dptr(pw.w), _dptr(pw.scales),
-                                 _dptr(pw.zeros), _dptr(residual), T, pw.N, pw.K, pw.bits, GROUP,
+                                 _dptr(pw.zeros), _dptr(residual), T, pw.N, pw.K, pw.bits, pw.group,
                                  _dptr(out), _stream(stream)), "w4_linear_route")
     return out
+
+
+# ------------------------------------------------------------------ bf16 activations
+
+def _workspace(workspace, T: int, K: int, like):
+    import torch
+    nbytes = bf16_workspace_bytes(T, K)
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=like.device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != like.device or \
+            not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a contiguous tensor of >= {nbytes} bytes on {like.device}")
+    return workspace
+
+
+def _bf16_call(route_id: int, op: int, x, pw: PackedWeight, residual, out, workspace, stream):
+    import torch
+    if (op == OP_SWIGLU) != pw.pair:
+        raise ValueError("the SwiGLU op takes a gate/up pair from pack_pair; the others a single matrix")
+    _check_x(x, pw.K, torch.bfloat16)
+    _check_weight(pw, x.device)
+    T = x.shape[0]
+    if op == OP_ADD:
+        _check_residual(residual, T, pw.N, x)
+    else:
+        residual = None
+    out = _out(out, T, pw.N, x)
+    ws = _workspace(workspace, T, pw.K, x)
+    nbytes = ws.numel() * ws.element_size()
+    args = (_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros))
+    L = lib()
+    if route_id >= 0:
+        st = L.w4_linear_route_bf16(route_id, op, *args, _dptr(residual), T, pw.N, pw.K, pw.bits,
+                                    pw.group, _dptr(out), _dptr(ws), nbytes, _stream(stream))
+    elif op == OP_SWIGLU:
+        st = L.w4_linear_swiglu_bf16(*args, T, pw.N, pw.K, pw.bits, pw.group, _dptr(out), _dptr(ws),
+                                     nbytes, _stream(stream))
+    elif op == OP_ADD:
+        st = L.w4_linear_add_bf16(*args, _dptr(residual), T, pw.N, pw.K, pw.bits, pw.group, _dptr(out),
+                                  _dptr(ws), nbytes, _stream(stream))
+    else:
+        st = L.w4_linear_bf16(*args, T, pw.N, pw.K, pw.bits, pw.group, _dptr(out), _dptr(ws), nbytes,
+                              _stream(stream))
+    _check(st, "w4_linear*_bf16")
+    return out
+
+
+def linear_bf16(x, pw: PackedWeight, out=None, workspace=None, stream=None):
+    """out[T, N] = x . dequant(W)^T with bf16 x and out, via ``w4_linear_bf16``.  workspace: a
+    device byte tensor of >= bf16_workspace_bytes(T, K) bytes (allocated here if None)."""
+    return _bf16_call(-1, OP_LINEAR, x, pw, None, out, workspace, stream)
+
+
+def linear_swiglu_bf16(x, pw: PackedWeight, out=None, workspace=None, stream=None):
+    return _bf16_call(-1, OP_SWIGLU, x, pw, None, out, workspace, stream)
+
+
+def linear_add_bf16(x, pw: PackedWeight, residual, out=None, workspace=None, stream=None):
+    return _bf16_call(-1, OP_ADD, x, pw, residual, out, workspace, stream)
+
+
+def linear_route_bf16(route_id: int, op: int, x, pw: PackedWeight, residual=None, out=None,
+                      workspace=None, stream=None):
+    """Run one specific route with bf16 activations (per-route parity tests)."""
+    if route_id < 0:
+        raise ValueError("route id must be >= 0")
+    return _bf16_call(route_id, op, x, pw, residual, out, workspace, stream)
 
 
 def route_for(op: int, bits: int, T: int, N: int, K: int) -> int:

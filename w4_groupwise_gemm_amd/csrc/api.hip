@@ -60,10 +60,10 @@ bool op_ok(int op) { return op == W4_OP_LINEAR || op == W4_OP_SWIGLU || op == W4
 int check_shape(int op, int T, int N, int K, int bits, int group) {
   if (!op_ok(op)) return W4_ERR_UNSUPPORTED;
   if (bits != 4 && bits != 5) return W4_ERR_UNSUPPORTED;
-  if (group != w4layout::kGroup) return W4_ERR_UNSUPPORTED;
+  if (!w4layout::group_ok(group)) return W4_ERR_UNSUPPORTED;
   if (T < 0 || N <= 0 || K <= 0) return W4_ERR_INVALID_ARG;
   if (T > kMaxDim || N > kMaxDim || K > kMaxDim) return W4_ERR_INVALID_ARG;
-  if (N % w4layout::kRowTile || K % w4layout::kGroup) return W4_ERR_INVALID_ARG;
+  if (N % w4layout::kRowTile || K % w4layout::k_multiple(group)) return W4_ERR_INVALID_ARG;
   return W4_OK;
 }
 
@@ -153,8 +153,11 @@ int pick_route(int op, int bits, int T, int N, int K) {
   return R_WIDE;
 }
 
+// xexp: nullptr for fp16 activations and outputs; for bf16 ones, x is the prepared fp16 copy and
+// xexp its per-token exponents (outputs and residual are then bf16).
 int launch_route(int route, int op, const void* x, const void* w, const void* s, const void* z,
-                 const void* res, int T, int N, int K, int bits, void* out, void* stream) {
+                 const void* res, int T, int N, int K, int bits, int group, void* out,
+                 void* stream, const int* xexp = nullptr) {
   const Route& R = kRoutes[route];
   if (T < R.tmin || T > R.tmax) return W4_ERR_DOMAIN;
   w4::KArgs a;
@@ -169,6 +172,8 @@ int launch_route(int route, int op, const void* x, const void* w, const void* s,
   a.K = K;
   a.KB = w4layout::num_kblocks(K);
   a.ldo = N;
+  a.szw = w4layout::sz_words(group);
+  a.xexp = xexp;
   const int epi = op == W4_OP_SWIGLU ? w4dev::EPI_SWIGLU
                   : op == W4_OP_ADD  ? w4dev::EPI_ADD
                                      : w4dev::EPI_STORE;
@@ -203,7 +208,49 @@ int run_op(int route, int op, const void* x, const void* w, const void* s, const
   if (T < kRoutes[route].tmin || T > kRoutes[route].tmax) return W4_ERR_DOMAIN;
   st = device_check();
   if (st != W4_OK) return st;
-  return launch_route(route, op, x, w, s, z, res, T, N, K, bits, out, stream);
+  return launch_route(route, op, x, w, s, z, res, T, N, K, bits, group, out, stream);
+}
+
+constexpr size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+// Workspace of a bf16 call: the fp16 copy of X (T x K) and the T per-token exponents.
+size_t bf16_ws_bytes(int T, int K) { return align16((size_t)T * K * 2) + align16((size_t)T * 4); }
+
+// bf16 activations: validate as the fp16 op (the tensors have the same sizes) plus the workspace,
+// then enqueue the preparation kernel (X[t] * 2^-e_t in fp16, and e_t) and the route's kernel.
+int run_op_bf16(int route, int op, const void* x, const void* w, const void* s, const void* z,
+                const void* res, int T, int N, int K, int bits, int group, void* out, void* ws,
+                size_t ws_bytes, void* stream) {
+  int st = validate(op, x, w, s, z, res, T, N, K, bits, group, out);
+  if (st != W4_OK) return st;
+  if (route < 0) route = pick_route(op, bits, T, N, K);
+  if (route >= kNumRoutes) return W4_ERR_DOMAIN;
+  if (T == 0) return W4_OK;
+  if (T < kRoutes[route].tmin || T > kRoutes[route].tmax) return W4_ERR_DOMAIN;
+  if (!ws) return W4_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return W4_ERR_MISALIGNED;
+  const size_t need = bf16_ws_bytes(T, K);
+  if (ws_bytes < need) return W4_ERR_INVALID_ARG;
+  const int rows = op == W4_OP_SWIGLU ? 2 * N : N;
+  auto rng = [](const void* p, size_t n) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+    return Range{b, b + n};
+  };
+  const Range rw = rng(ws, need);
+  if (overlap(rw, rng(x, (size_t)T * K * 2)) || overlap(rw, rng(out, (size_t)T * N * 2)) ||
+      overlap(rw, rng(w, w4_packed_bytes(rows, K, bits, group))) ||
+      overlap(rw, rng(s, w4_packed_sz_bytes(rows, K, group))) ||
+      overlap(rw, rng(z, w4_packed_sz_bytes(rows, K, group))) ||
+      (op == W4_OP_ADD && overlap(rw, rng(res, (size_t)T * N * 2))))
+    return W4_ERR_ALIAS;
+  st = device_check();
+  if (st != W4_OK) return st;
+  _Float16* xh = static_cast<_Float16*>(ws);
+  int* xexp = reinterpret_cast<int*>(static_cast<char*>(ws) + align16((size_t)T * K * 2));
+  if (w4::launch_bf16_prep(static_cast<const uint16_t*>(x), T, K, xh, xexp,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
+    return W4_ERR_LAUNCH;
+  return launch_route(route, op, xh, w, s, z, res, T, N, K, bits, group, out, stream, xexp);
 }
 
 }  // namespace
@@ -272,6 +319,8 @@ extern "C" int w4_linear_grouped(const uint16_t* x, const w4_parent* parents, in
       a.K = K;
       a.KB = w4layout::num_kblocks(K);
       a.ldo = parents[p].N;
+      a.szw = w4layout::sz_words(group);
+      a.xexp = nullptr;
       g.bits[p] = parents[p].bits;
     }
     return w4::launch_grouped(g, static_cast<hipStream_t>(stream)) == hipSuccess ? W4_OK : W4_ERR_LAUNCH;
@@ -279,10 +328,48 @@ extern "C" int w4_linear_grouped(const uint16_t* x, const w4_parent* parents, in
   for (int p = 0; p < nparents; ++p) {
     const w4_parent& q = parents[p];
     const int e = launch_route(pick_route(W4_OP_LINEAR, q.bits, T, q.N, K), W4_OP_LINEAR, x, q.w, q.scales,
-                               q.zeros, nullptr, T, q.N, K, q.bits, q.out, stream);
+                               q.zeros, nullptr, T, q.N, K, q.bits, group, q.out, stream);
     if (e != W4_OK) return e;
   }
   return W4_OK;
+}
+
+extern "C" size_t w4_bf16_workspace_bytes(int T, int K) {
+  if (T < 0 || K <= 0 || T > kMaxDim || K > kMaxDim || K % 64) return 0;
+  return bf16_ws_bytes(T, K);
+}
+
+extern "C" int w4_linear_bf16(const uint16_t* x, const void* w, const uint16_t* scales,
+                              const uint16_t* zeros, int T, int N, int K, int bits, int group,
+                              uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_op_bf16(-1, W4_OP_LINEAR, x, w, scales, zeros, nullptr, T, N, K, bits, group, out,
+                     workspace, workspace_bytes, stream);
+}
+
+extern "C" int w4_linear_swiglu_bf16(const uint16_t* x, const void* w_pair,
+                                     const uint16_t* scales_pair, const uint16_t* zeros_pair, int T,
+                                     int N, int K, int bits, int group, uint16_t* out,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return run_op_bf16(-1, W4_OP_SWIGLU, x, w_pair, scales_pair, zeros_pair, nullptr, T, N, K, bits,
+                     group, out, workspace, workspace_bytes, stream);
+}
+
+extern "C" int w4_linear_add_bf16(const uint16_t* x, const void* w, const uint16_t* scales,
+                                  const uint16_t* zeros, const uint16_t* residual, int T, int N,
+                                  int K, int bits, int group, uint16_t* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return run_op_bf16(-1, W4_OP_ADD, x, w, scales, zeros, residual, T, N, K, bits, group, out,
+                     workspace, workspace_bytes, stream);
+}
+
+extern "C" int w4_linear_route_bf16(int route_id, int op, const uint16_t* x, const void* w,
+                                    const uint16_t* scales, const uint16_t* zeros,
+                                    const uint16_t* residual, int T, int N, int K, int bits,
+                                    int group, uint16_t* out, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  if (route_id < 0 || route_id >= kNumRoutes) return W4_ERR_DOMAIN;
+  return run_op_bf16(route_id, op, x, w, scales, zeros, residual, T, N, K, bits, group, out,
+                     workspace, workspace_bytes, stream);
 }
 
 extern "C" int w4_route_for(int op, int bits, int T, int N, int K) {

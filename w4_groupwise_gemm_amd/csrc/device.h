@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
 #include "layout.h"
 
 namespace w4dev {
@@ -101,14 +102,38 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float silu(float a) { return a / (1.0f + expf(-a)); }
 
-// Epilogue of one output quad: 4 consecutive output columns n..n+3 of token t.
-// out / res are fp16 [T][ldo]; the caller guarantees t < T and n + 3 < ldo.
+__device__ __forceinline__ float bf16_value(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+__device__ __forceinline__ uint16_t bf16_bits(float f) {  // round to nearest even
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Epilogue of one output quad: 4 consecutive output columns n..n+3 of token t (the caller
+// guarantees t < T and n + 3 < ldo).  fp16 activations: out = fp16(v) / fp16(silu(v) * up) /
+// fp16(v + res).  bf16 activations (a.xexp set): the sums were formed from X[t] * 2^-e, so they
+// are scaled by 2^e first, the residual is bf16, and the result is rounded to bf16.
 template <int EPI>
-__device__ __forceinline__ void store_quad(f16* out, const f16* res, size_t off, f32x4 v,
-                                           f32x4 up) {
+__device__ __forceinline__ void store_quad(const w4::KArgs& a, int t, int n, f32x4 v, f32x4 up) {
+  const size_t off = (size_t)t * a.ldo + n;
+  if (a.xexp) {
+    const int e = a.xexp[t];
+    uint16_t h[4];
+    const uint16_t* r16 = reinterpret_cast<const uint16_t*>(a.res);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float y = ldexpf(v[i], e);
+      if constexpr (EPI == EPI_ADD) y = y + bf16_value(r16[off + i]);
+      if constexpr (EPI == EPI_SWIGLU) y = silu(y) * ldexpf(up[i], e);
+      h[i] = bf16_bits(y);
+    }
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.out) + off) =
+        u32x2{(uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16)};
+    return;
+  }
   f16x4 h;
   if constexpr (EPI == EPI_ADD) {
-    const f16x4 r = *reinterpret_cast<const f16x4*>(res + off);
+    const f16x4 r = *reinterpret_cast<const f16x4*>(a.res + off);
     h[0] = (f16)(v[0] + (float)r[0]);
     h[1] = (f16)(v[1] + (float)r[1]);
     h[2] = (f16)(v[2] + (float)r[2]);
@@ -124,17 +149,27 @@ __device__ __forceinline__ void store_quad(f16* out, const f16* res, size_t off,
     h[2] = (f16)v[2];
     h[3] = (f16)v[3];
   }
-  *reinterpret_cast<f16x4*>(out + off) = h;
+  *reinterpret_cast<f16x4*>(a.out + off) = h;
 }
 
+// One output element (token t, column n), same rules.
 template <int EPI>
-__device__ __forceinline__ void store_one(f16* out, const f16* res, size_t off, float v, float up) {
+__device__ __forceinline__ void store_one(const w4::KArgs& a, int t, int n, float v, float up) {
+  const size_t off = (size_t)t * a.ldo + n;
+  if (a.xexp) {
+    const int e = a.xexp[t];
+    float y = ldexpf(v, e);
+    if constexpr (EPI == EPI_ADD) y = y + bf16_value(reinterpret_cast<const uint16_t*>(a.res)[off]);
+    if constexpr (EPI == EPI_SWIGLU) y = silu(y) * ldexpf(up, e);
+    reinterpret_cast<uint16_t*>(a.out)[off] = bf16_bits(y);
+    return;
+  }
   if constexpr (EPI == EPI_ADD) {
-    out[off] = (f16)(v + (float)res[off]);
+    a.out[off] = (f16)(v + (float)a.res[off]);
   } else if constexpr (EPI == EPI_SWIGLU) {
-    out[off] = (f16)(silu(v) * up);
+    a.out[off] = (f16)(silu(v) * up);
   } else {
-    out[off] = (f16)v;
+    a.out[off] = (f16)v;
   }
 }
 

@@ -22,18 +22,27 @@ inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, siz
 }
 
 struct KArgs {
-  const _Float16* x;     // [T][K] activations
+  const _Float16* x;     // [T][K] activations (fp16; bf16 inputs arrive here converted)
   const uint8_t* w;      // packed codes, `rows` packed rows
-  const uint32_t* sc;    // packed scales, one fp16 pair (2 groups) per (row tile, k-block, row)
+  const uint32_t* sc;    // packed scales: szw fp16 pairs per (row tile, k-block)
   const uint32_t* zr;    // packed zero-points, same layout
-  const _Float16* res;   // [T][ldo] residual (EPI_ADD) or nullptr
-  _Float16* out;         // [T][ldo]
+  const _Float16* res;   // [T][ldo] residual (EPI_ADD) or nullptr; bf16 bits when xexp is set
+  _Float16* out;         // [T][ldo]; bf16 bits when xexp is set
   int T;                 // tokens (>= 1)
   int rows;              // packed rows (2N for the SwiGLU pair)
   int K;                 // columns of X and W
   int KB;                // ceil(K / 128)
   int ldo;               // output columns (N)
+  int szw;               // 32-bit scale / zero-point words per (row tile, k-block): 16, or 32 for groups of 32
+  const int* xexp;       // bf16 activations: x holds X[t] * 2^-xexp[t] in fp16, and out / res are
+                         // bf16 (the epilogue scales by 2^xexp[t]); nullptr for fp16 in and out
 };
+
+// Word, inside the scale / zero-point block of a (row tile, k-block), of the pair that row r
+// needs when its codes come from lane group g (see w4layout::sz_word).
+__device__ __forceinline__ int sz_lane_word(const KArgs& a, int r, int g) {
+  return a.szw == 32 ? 16 * (g >> 1) + r : r;
+}
 
 // Several matrices sharing one activation (same x, T and K), each with its own output.
 constexpr int kMaxParents = 4;
@@ -110,6 +119,8 @@ inline hipError_t launch_stream16(int bits, int epi, const KArgs& a, hipStream_t
 }
 // narrow: token tiles of tn (32 or 64) columns; T > tn runs ceil(T / tn) token blocks side by side
 hipError_t launch_narrow(int tn, int bits, int epi, const KArgs& a, hipStream_t stream);
+// bf16 activations [T][K] -> fp16 X[t] * 2^-e_t in xh and e_t in xexp (bf16.hip)
+hipError_t launch_bf16_prep(const uint16_t* x, int T, int K, _Float16* xh, int* xexp, hipStream_t stream);
 hipError_t launch_wide(int bits, int epi, const KArgs& a, hipStream_t stream);    // any T
 hipError_t launch_splitk(int bits, int epi, const KArgs& a, hipStream_t stream);  // T <= 32
 

@@ -39,15 +39,16 @@ using namespace t32;
 using w4layout::block_bytes;
 
 // Byte layout of one code stage: NP pairs x 2 tiles of 1 KB low-plane codes (64 lanes x 16 B,
-// as in the packed block), then (5-bit) 2 NP x 256 B high planes, then 256 B of scale pairs and
-// 256 B of zero-point pairs (lane 16 i + r of the load = tile i, row r).
+// as in the packed block), then (5-bit) 2 NP x 256 B high planes, then the scale words and the
+// zero-point words of the 2 NP tiles, each tile's (tile, k-block) block in turn (64 bytes, or
+// 128 for groups of 32; room is kept for 128).
 template <int BITS, int NP>
 struct CodeStage {
   static constexpr int kLo = 0;
   static constexpr int kHi = NP * 2 * 1024;
   static constexpr int kS = kHi + (BITS == 5 ? NP * 2 * 256 : 0);
-  static constexpr int kZ = kS + 256;
-  static constexpr int kBytes = kZ + 256;
+  static constexpr int kZ = kS + NP * 2 * 128;
+  static constexpr int kBytes = kZ + NP * 2 * 128;
   // direct-to-LDS instructions the code producer issues per block
   static constexpr int kOps = NP * 2 * (BITS == 5 ? 2 : 1) + 2;
 };
@@ -88,12 +89,16 @@ __device__ __forceinline__ void load_codes(const Rsrcs& R, const KArgs& a, char*
     lds_load16(R.w, st + CS::kLo + i * 1024, bi * BLK + lane * 16);
     if constexpr (BITS == 5) lds_load4(R.w, st + CS::kHi + i * 256, bi * BLK + 1024 + lane * 4);
   }
-  // scales / zero-points: lane 16 i + r takes tile i, row r (lanes past 2 NP tiles re-read the
-  // last tile; their LDS words are never read)
-  const int tile = min(2 * pair0 + min(lane >> 4, 2 * NP - 1), ntiles - 1);
-  const int off = (tile * a.KB + kb) * 64 + (lane & 15) * 4;
-  lds_load4(R.s, st + CS::kS, off);
-  lds_load4(R.z, st + CS::kZ, off);
+  // scales / zero-points: the 2 NP tiles' blocks of szb bytes each, 16 bytes per lane, by the
+  // lanes that cover them (at least 8 of the 64: one instruction each, whatever the group
+  // size); tiles past the last one re-read it, and those words are never read
+  const int szb = 4 * a.szw;
+  if (lane * 16 < 2 * NP * szb) {
+    const int tile = min(2 * pair0 + lane * 16 / szb, ntiles - 1);
+    const int off = (tile * a.KB + kb) * szb + lane * 16 % szb;
+    lds_load16(R.s, st + CS::kS, off);
+    lds_load16(R.z, st + CS::kZ, off);
+  }
 }
 
 // Activation tile of block kb, BN token rows x 256 bytes: BN / 4 direct-to-LDS instructions of
@@ -173,7 +178,7 @@ __device__ __forceinline__ void consume(const KArgs& a, const char* cring, const
   using F = Frag<BITS, NP, NTT, ST::kN>;
   constexpr int BN = 32 * NTT, XB = BN * 256;
   const int lane = threadIdx.x & 63;
-  const LaneMap m = lane_map(lane);
+  const LaneMap m = lane_map(a, lane);
   const uint32_t magic = vgpr_const(0x64006400u);
   const int brow = lane & 31;
   const int bsw = brow * 256 + 16 * ((4 * (lane >> 5)) ^ (brow & 15));
@@ -181,7 +186,8 @@ __device__ __forceinline__ void consume(const KArgs& a, const char* cring, const
   // lane-constant byte offsets inside a code stage
   const int lo_off = CS::kLo + m.th * 1024 + slot + 4 * ST::kJ0;
   const int hi_off = CS::kHi + m.th * 256 + slot / 4;
-  const int sz_off = m.th * 64 + m.row4;
+  const int szb = 4 * a.szw;  // bytes of one tile's scale (or zero-point) block
+  const int sz_off = m.th * szb + m.szoff;
   const int KB = a.KB;
   const bool half_last = (KB * 128 != a.K);  // last block holds one group only
 
@@ -192,8 +198,8 @@ __device__ __forceinline__ void consume(const KArgs& a, const char* cring, const
     for (int p = 0; p < NP; ++p) {
       f.cw[p] = *reinterpret_cast<const typename CWd::T*>(cs + lo_off + p * 2048);
       f.hw[p] = BITS == 5 ? *reinterpret_cast<const uint32_t*>(cs + hi_off + p * 512) : 0u;
-      f.sp[p] = *reinterpret_cast<const uint32_t*>(cs + CS::kS + sz_off + p * 128);
-      f.zp[p] = *reinterpret_cast<const uint32_t*>(cs + CS::kZ + sz_off + p * 128);
+      f.sp[p] = *reinterpret_cast<const uint32_t*>(cs + CS::kS + sz_off + p * 2 * szb);
+      f.zp[p] = *reinterpret_cast<const uint32_t*>(cs + CS::kZ + sz_off + p * 2 * szb);
     }
     load_b<NTT, 2 * ST::kJ0 + ST::kS>(xs, bsw, f.B[0]);
     if constexpr (ST::kN == 2) load_b<NTT, 2 * (ST::kJ0 + 1) + ST::kS>(xs, bsw, f.B[ST::kN - 1]);
@@ -250,6 +256,7 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
     a.x += t0 * a.K;
     a.out += t0 * a.ldo;
     if (a.res) a.res += t0 * a.ldo;
+    if (a.xexp) a.xexp += t0;
     a.T -= (int)t0;
   }
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -264,8 +271,8 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
   Rsrcs R;
   R.x = rsrc(a.x, (uint32_t)((size_t)a.T * a.K * 2));
   R.w = rsrc(a.w, (uint32_t)((size_t)ntiles * KB * block_bytes(BITS)));
-  R.s = rsrc(a.sc, (uint32_t)((size_t)ntiles * KB * 64));
-  R.z = rsrc(a.zr, (uint32_t)((size_t)ntiles * KB * 64));
+  R.s = rsrc(a.sc, (uint32_t)((size_t)ntiles * KB * 4 * a.szw));
+  R.z = rsrc(a.zr, (uint32_t)((size_t)ntiles * KB * 4 * a.szw));
   int voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -286,8 +293,8 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
 #pragma unroll
     for (int j = 0; j < DX; ++j) load_x<BN>(R, a, xring + j * XB, voff, min(j, KB - 1));
   } else {
-    const int zbase = 2 * pair0 * KB * 64;  // bytes: zero-points of the workgroup's tiles
-    const int zbytes = 2 * NP * KB * 64;
+    const int zbase = 2 * pair0 * KB * 4 * a.szw;  // bytes: zero-points of the workgroup's tiles
+    const int zbytes = 2 * NP * KB * 4 * a.szw;
     const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f};
     constexpr int STEP = 64 * NC * 16;  // bytes per load instruction of all consumers
     bool exact = true;
@@ -383,7 +390,7 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
       if (t >= a.T || 2 * pair >= ntiles) continue;
       const f32x4 g = {sum(p, tt, 4 * q), sum(p, tt, 4 * q + 1), sum(p, tt, 4 * q + 2), sum(p, tt, 4 * q + 3)};
       const f32x4 u = {sum(p, tt, 8 + 4 * q), sum(p, tt, 9 + 4 * q), sum(p, tt, 10 + 4 * q), sum(p, tt, 11 + 4 * q)};
-      store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + 16 * pair + 8 * q + 4 * h, g, u);
+      store_quad<EPI>(a, t, 16 * pair + 8 * q + 4 * h, g, u);
     }
   } else {
     // (item, register quad q) pairs: pair rows 8q + 4h + 0..3
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
       if (t >= a.T || 2 * pair >= ntiles) continue;
       if (q >= 2 && 2 * pair + 1 >= ntiles) continue;  // odd tile count: no second tile
       const f32x4 v = {sum(p, tt, 4 * q), sum(p, tt, 4 * q + 1), sum(p, tt, 4 * q + 2), sum(p, tt, 4 * q + 3)};
-      store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + 32 * pair + 8 * q + 4 * h, v, f32x4{});
+      store_quad<EPI>(a, t, 32 * pair + 8 * q + 4 * h, v, f32x4{});
     }
   }
 }

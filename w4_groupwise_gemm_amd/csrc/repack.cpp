@@ -18,8 +18,8 @@ namespace {
 using namespace w4layout;
 
 bool shape_ok(int N, int K, int bits, int group) {
-  return N > 0 && K > 0 && (N % kRowTile) == 0 && (K % kGroup) == 0 &&
-         (bits == 4 || bits == 5) && group == kGroup;
+  return N > 0 && K > 0 && (N % kRowTile) == 0 && group_ok(group) && (K % k_multiple(group)) == 0 &&
+         (bits == 4 || bits == 5);
 }
 
 inline int canonical_code(const uint8_t* lo, const uint8_t* hi, int K, int n, int k, int bits) {
@@ -31,10 +31,10 @@ inline int canonical_code(const uint8_t* lo, const uint8_t* hi, int K, int n, in
 
 // Repack source row tile `src_rt` of one canonical matrix into destination row tile `dst_rt`.
 void repack_tile(const uint8_t* lo, const uint8_t* hi, const uint16_t* scales,
-                 const uint16_t* zeros, int K, int bits, int src_rt, int dst_rt, uint8_t* w_out,
-                 uint16_t* s_out, uint16_t* z_out) {
+                 const uint16_t* zeros, int K, int bits, int group, int src_rt, int dst_rt,
+                 uint8_t* w_out, uint16_t* s_out, uint16_t* z_out) {
   const int KB = num_kblocks(K);
-  const int G = K / kGroup;
+  const int G = K / group;
   const size_t blk = block_bytes(bits);
   for (int kb = 0; kb < KB; ++kb) {
     uint8_t* block = w_out + ((size_t)dst_rt * KB + kb) * blk;
@@ -54,13 +54,19 @@ void repack_tile(const uint8_t* lo, const uint8_t* hi, const uint16_t* scales,
       }
       if (bits == 5) std::memcpy(block + 64 * 16 + lane * 4, &hiword, 4);
     }
+    // scale / zero-point words: word sz_word(group, r, g) of the block holds, in half h, the
+    // group of the codes that row r's lane group g holds in its dwords 2h and 2h + 1 (columns
+    // 64 h + 16 g .. 64 h + 16 g + 15 of the block)
+    const int W = sz_words(group);
     for (int r = 0; r < kRowTile; ++r) {
       const int n = src_rt * kRowTile + r;
-      for (int h = 0; h < 2; ++h) {
-        const int grp = 2 * kb + h;
-        const size_t o = (((size_t)dst_rt * KB + kb) * kRowTile + r) * 2 + h;
-        s_out[o] = grp < G ? scales[(size_t)n * G + grp] : 0;
-        z_out[o] = grp < G ? zeros[(size_t)n * G + grp] : 0;
+      for (int g = 0; g < 4; ++g) {
+        for (int h = 0; h < 2; ++h) {
+          const int grp = (kBlockK * kb + 64 * h + 16 * g) / group;
+          const size_t o = (((size_t)dst_rt * KB + kb) * W + sz_word(group, r, g)) * 2 + h;
+          s_out[o] = grp < G ? scales[(size_t)n * G + grp] : 0;
+          z_out[o] = grp < G ? zeros[(size_t)n * G + grp] : 0;
+        }
       }
     }
   }
@@ -75,21 +81,21 @@ extern "C" size_t w4_packed_bytes(int N, int K, int bits, int group) {
 
 extern "C" size_t w4_packed_sz_bytes(int N, int K, int group) {
   if (!shape_ok(N, K, 4, group)) return 0;
-  return (size_t)(N / kRowTile) * num_kblocks(K) * kRowTile * 2 * sizeof(uint16_t);
+  return (size_t)(N / kRowTile) * num_kblocks(K) * sz_words(group) * 2 * sizeof(uint16_t);
 }
 
 extern "C" int w4_repack(const uint8_t* codes_lo, const uint8_t* codes_hi, const uint16_t* scales,
                          const uint16_t* zeros, int N, int K, int bits, int group, void* w_out,
                          uint16_t* scales_out, uint16_t* zeros_out) {
   if (bits != 4 && bits != 5) return W4_ERR_UNSUPPORTED;
-  if (group != kGroup) return W4_ERR_UNSUPPORTED;
+  if (!group_ok(group)) return W4_ERR_UNSUPPORTED;
   if (!shape_ok(N, K, bits, group)) return W4_ERR_INVALID_ARG;
   if (!codes_lo || !scales || !zeros || !w_out || !scales_out || !zeros_out)
     return W4_ERR_INVALID_ARG;
   if ((bits == 5) != (codes_hi != nullptr)) return W4_ERR_INVALID_ARG;
   for (int rt = 0; rt < N / kRowTile; ++rt)
-    repack_tile(codes_lo, codes_hi, scales, zeros, K, bits, rt, rt, (uint8_t*)w_out, scales_out,
-                zeros_out);
+    repack_tile(codes_lo, codes_hi, scales, zeros, K, bits, group, rt, rt, (uint8_t*)w_out,
+                scales_out, zeros_out);
   return W4_OK;
 }
 
@@ -100,7 +106,7 @@ extern "C" int w4_repack_pair(const uint8_t* gate_lo, const uint8_t* gate_hi,
                               int bits, int group, void* w_pair_out, uint16_t* scales_pair_out,
                               uint16_t* zeros_pair_out) {
   if (bits != 4 && bits != 5) return W4_ERR_UNSUPPORTED;
-  if (group != kGroup) return W4_ERR_UNSUPPORTED;
+  if (!group_ok(group)) return W4_ERR_UNSUPPORTED;
   if (!shape_ok(N, K, bits, group)) return W4_ERR_INVALID_ARG;
   if (!gate_lo || !gate_scales || !gate_zeros || !up_lo || !up_scales || !up_zeros ||
       !w_pair_out || !scales_pair_out || !zeros_pair_out)
@@ -108,10 +114,10 @@ extern "C" int w4_repack_pair(const uint8_t* gate_lo, const uint8_t* gate_hi,
   if ((bits == 5) != (gate_hi != nullptr) || (bits == 5) != (up_hi != nullptr))
     return W4_ERR_INVALID_ARG;
   for (int rt = 0; rt < N / kRowTile; ++rt) {
-    repack_tile(gate_lo, gate_hi, gate_scales, gate_zeros, K, bits, rt, 2 * rt,
+    repack_tile(gate_lo, gate_hi, gate_scales, gate_zeros, K, bits, group, rt, 2 * rt,
                 (uint8_t*)w_pair_out, scales_pair_out, zeros_pair_out);
-    repack_tile(up_lo, up_hi, up_scales, up_zeros, K, bits, rt, 2 * rt + 1, (uint8_t*)w_pair_out,
-                scales_pair_out, zeros_pair_out);
+    repack_tile(up_lo, up_hi, up_scales, up_zeros, K, bits, group, rt, 2 * rt + 1,
+                (uint8_t*)w_pair_out, scales_pair_out, zeros_pair_out);
   }
   return W4_OK;
 }

@@ -53,8 +53,8 @@ __device__ __forceinline__ void issue(Blk<NP>& b, const Rsrcs& R, const KArgs& a
       b.cw[p][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.w, bi * BLK + m.slot16[s], 0, 0));
       b.hw[p][s] = BITS == 5 ? __builtin_amdgcn_raw_buffer_load_b32(R.w, bi * BLK + 1024 + m.slot16[s] / 4, 0, 0) : 0u;
     }
-    b.sp[p] = __builtin_amdgcn_raw_buffer_load_b32(R.s, bi * 64 + m.row4, 0, 0);
-    b.zp[p] = __builtin_amdgcn_raw_buffer_load_b32(R.z, bi * 64 + m.row4, 0, 0);
+    b.sp[p] = __builtin_amdgcn_raw_buffer_load_b32(R.s, bi * 4 * a.szw + m.szoff, 0, 0);
+    b.zp[p] = __builtin_amdgcn_raw_buffer_load_b32(R.z, bi * 4 * a.szw + m.szoff, 0, 0);
   }
   // step i = 2 J + S covers k = 64 (J / 2) + 16 (S + 2 h) + 8 (J % 2) + 0..7 of the block
 #pragma unroll
@@ -98,13 +98,13 @@ __global__ __launch_bounds__(NW * 64) void splitk_kernel(KArgs a) {
   const int kb0 = (KB * wave) / NW, kb1 = (KB * (wave + 1)) / NW;
   const bool half_last = (KB * 128 != a.K);
   const uint32_t magic = vgpr_const(0x64006400u);
-  const LaneMap m = lane_map(lane);
+  const LaneMap m = lane_map(a, lane);
 
   Rsrcs R;
   R.x = rsrc(a.x, (uint32_t)((size_t)a.T * a.K * 2));
   R.w = rsrc(a.w, (uint32_t)((size_t)ntiles * KB * block_bytes(BITS)));
-  R.s = rsrc(a.sc, (uint32_t)((size_t)ntiles * KB * 64));
-  R.z = rsrc(a.zr, (uint32_t)((size_t)ntiles * KB * 64));
+  R.s = rsrc(a.sc, (uint32_t)((size_t)ntiles * KB * 4 * a.szw));
+  R.z = rsrc(a.zr, (uint32_t)((size_t)ntiles * KB * 4 * a.szw));
   // lane's activation row (token lane % 32) and k half (32 (lane / 32)), in bytes
   const int xoff = ((lane & 31) * a.K + 32 * (lane >> 5)) * 2;
 
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(NW * 64) void splitk_kernel(KArgs a) {
       if (2 * pair >= ntiles) continue;
       const f32x4 g = {sum(p, 4 * q), sum(p, 4 * q + 1), sum(p, 4 * q + 2), sum(p, 4 * q + 3)};
       const f32x4 u = {sum(p, 8 + 4 * q), sum(p, 9 + 4 * q), sum(p, 10 + 4 * q), sum(p, 11 + 4 * q)};
-      store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + 16 * pair + 8 * q + 4 * h, g, u);
+      store_quad<EPI>(a, t, 16 * pair + 8 * q + 4 * h, g, u);
     }
   } else {
     for (int idx = wave; idx < NP * 4; idx += NW) {
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(NW * 64) void splitk_kernel(KArgs a) {
       if (2 * pair >= ntiles) continue;
       if (q >= 2 && 2 * pair + 1 >= ntiles) continue;  // odd tile count: no second tile
       const f32x4 v = {sum(p, 4 * q), sum(p, 4 * q + 1), sum(p, 4 * q + 2), sum(p, 4 * q + 3)};
-      store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + 32 * pair + 8 * q + 4 * h, v, f32x4{});
+      store_quad<EPI>(a, t, 32 * pair + 8 * q + 4 * h, v, f32x4{});
     }
   }
 }

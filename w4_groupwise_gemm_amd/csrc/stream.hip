@@ -117,6 +117,7 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
+  const int szl = sz_lane_word(a, r, g);  // the lane's scale / zero-point word in a block
   const int ntiles = a.rows / 16;
   const int tile0 = bx * RT;
   // local block index c of this wave is k-block wave + NW * c; nbw of them
@@ -245,8 +246,8 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
           R.hw[i][rt] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(a.w + bi * BLK + 1024 + lane * 4));
         else
           R.hw[i][rt] = 0;
-        R.sp[i][rt] = a.sc[bi * 16 + r];
-        R.zp[i][rt] = a.zr[bi * 16 + r];
+        R.sp[i][rt] = a.sc[bi * a.szw + szl];
+        R.zp[i][rt] = a.zr[bi * a.szw + szl];
       }
       if constexpr (XL == 0) {
         const bool half_block = HB && (kb * 128 + 64 >= a.K);
@@ -445,12 +446,12 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
       if constexpr (EPI == EPI_SWIGLU) {
         const int gtile = tile0 + 2 * p;
         if (gtile >= ntiles) continue;
-        store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + (gtile >> 1) * 16 + 4 * (l >> 4), sum(h, 2 * p, l),
+        store_quad<EPI>(a, t, (gtile >> 1) * 16 + 4 * (l >> 4), sum(h, 2 * p, l),
                         sum(h, 2 * p + 1, l));
       } else {
         const int tile = tile0 + p;
         if (tile >= ntiles) continue;
-        store_quad<EPI>(a.out, a.res, (size_t)t * a.ldo + tile * 16 + 4 * (l >> 4), sum(h, p, l), f32x4{});
+        store_quad<EPI>(a, t, tile * 16 + 4 * (l >> 4), sum(h, p, l), f32x4{});
       }
     }
   } else {
@@ -477,13 +478,13 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
           gv += red[((w * RT + 2 * p) * 4 + t) * 16 + row];
           uv += red[((w * RT + 2 * p + 1) * 4 + t) * 16 + row];
         }
-        store_one<EPI>(a.out, a.res, (size_t)t * a.ldo + (gtile >> 1) * 16 + row, gv, uv);
+        store_one<EPI>(a, t, (gtile >> 1) * 16 + row, gv, uv);
       } else {
         const int tile = tile0 + p;
         if (tile >= ntiles) continue;
         float v = red[(p * 4 + t) * 16 + row];
         for (int w = 1; w < NW; ++w) v += red[((w * RT + p) * 4 + t) * 16 + row];
-        store_one<EPI>(a.out, a.res, (size_t)t * a.ldo + tile * 16 + row, v, 0.f);
+        store_one<EPI>(a, t, tile * 16 + row, v, 0.f);
       }
     }
   }

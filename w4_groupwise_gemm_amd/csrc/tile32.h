@@ -47,13 +47,15 @@ struct Rsrcs {
 struct LaneMap {
   int slot16[2];  // byte offset of the lane's 16-byte code slot in a block, sets 0 and 1
   int th;         // tile of the pair (0 / 1) this lane reads
-  int row4;       // 4 * (row within the tile): scale / zero-point slot
+  int szoff;      // byte offset of the lane's scale / zero-point pair in a (tile, k-block) block
 };
 
-__device__ __forceinline__ LaneMap lane_map(int lane) {
+// The lane's source lane groups S + 2 (lane / 32), S = 0, 1, fall in one half of the lane
+// groups, so one scale / zero-point pair serves both code sets for every group size.
+__device__ __forceinline__ LaneMap lane_map(const KArgs& a, int lane) {
   LaneMap m;
   m.th = (lane >> 4) & 1;
-  m.row4 = (lane & 15) * 4;
+  m.szoff = 4 * sz_lane_word(a, lane & 15, 2 * (lane >> 5));
 #pragma unroll
   for (int s = 0; s < 2; ++s) m.slot16[s] = ((lane & 15) + 16 * (s + 2 * (lane >> 5))) * 16;
   return m;
@@ -104,18 +106,17 @@ __device__ __forceinline__ void store_pair(const KArgs& a, const f32x16& v, int 
   const int t = tok + (lane & 31);
   if (t >= a.T || 2 * pair >= ntiles) return;
   const int h = lane >> 5;
-  const size_t rowoff = (size_t)t * a.ldo;
   if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int q = 0; q < 2; ++q)
-      store_quad<EPI>(a.out, a.res, rowoff + 16 * pair + 8 * q + 4 * h,
+      store_quad<EPI>(a, t, 16 * pair + 8 * q + 4 * h,
                       f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]},
                       f32x4{v[8 + 4 * q], v[9 + 4 * q], v[10 + 4 * q], v[11 + 4 * q]});
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (q >= 2 && 2 * pair + 1 >= ntiles) break;  // odd tile count: no second tile
-      store_quad<EPI>(a.out, a.res, rowoff + 32 * pair + 8 * q + 4 * h,
+      store_quad<EPI>(a, t, 32 * pair + 8 * q + 4 * h,
                       f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]}, f32x4{});
     }
   }

@@ -76,8 +76,8 @@ __device__ __forceinline__ void load_pair(PairCodes<BITS>& c, const Rsrcs& R, co
     else
       c.hw[s] = 0;
   }
-  c.sp = __builtin_amdgcn_raw_buffer_load_b32(R.s, bi * 64 + m.row4, 0, 0);
-  c.zp = __builtin_amdgcn_raw_buffer_load_b32(R.z, bi * 64 + m.row4, 0, 0);
+  c.sp = __builtin_amdgcn_raw_buffer_load_b32(R.s, bi * 4 * a.szw + m.szoff, 0, 0);
+  c.zp = __builtin_amdgcn_raw_buffer_load_b32(R.z, bi * 4 * a.szw + m.szoff, 0, 0);
 }
 
 // Wave W's share of pair `pair`: set S = W / 2, dwords j = 2 (W % 2) and 2 (W % 2) + 1.
@@ -93,8 +93,8 @@ __device__ __forceinline__ void load_share(ShareCodes<BITS>& c, const Rsrcs& R, 
     c.hw = __builtin_amdgcn_raw_buffer_load_b32(R.w, bi * BLK + 1024 + slot / 4, 0, 0);
   else
     c.hw = 0;
-  c.sp = __builtin_amdgcn_raw_buffer_load_b32(R.s, bi * 64 + m.row4, 0, 0);
-  c.zp = __builtin_amdgcn_raw_buffer_load_b32(R.z, bi * 64 + m.row4, 0, 0);
+  c.sp = __builtin_amdgcn_raw_buffer_load_b32(R.s, bi * 4 * a.szw + m.szoff, 0, 0);
+  c.zp = __builtin_amdgcn_raw_buffer_load_b32(R.z, bi * 4 * a.szw + m.szoff, 0, 0);
 }
 
 // k-steps of a block, in group order: index i = 2 J + S is the 16-k step (J, S); steps 0..3
@@ -229,13 +229,13 @@ __global__ __launch_bounds__(256, OCC) void wide_kernel(KArgs a, int nrb, int nt
   const int tok0 = tb * BN;
   const int pair = rb * NP + wave, spair = rb * NP + 4;
   const uint32_t magic = vgpr_const(0x64006400u);
-  const LaneMap m = lane_map(lane);
+  const LaneMap m = lane_map(a, lane);
 
   Rsrcs R;
   R.x = rsrc(a.x, (uint32_t)((size_t)a.T * a.K * 2));
   R.w = rsrc(a.w, (uint32_t)((size_t)ntiles * a.KB * block_bytes(BITS)));
-  R.s = rsrc(a.sc, (uint32_t)((size_t)ntiles * a.KB * 64));
-  R.z = rsrc(a.zr, (uint32_t)((size_t)ntiles * a.KB * 64));
+  R.s = rsrc(a.sc, (uint32_t)((size_t)ntiles * a.KB * 4 * a.szw));
+  R.z = rsrc(a.zr, (uint32_t)((size_t)ntiles * a.KB * 4 * a.szw));
   int voff[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -262,8 +262,8 @@ __global__ __launch_bounds__(256, OCC) void wide_kernel(KArgs a, int nrb, int nt
   // paths (a per-block branch would make the register allocator hold both at once).
   bool exact = true;
   {
-    const int zbase = rb * TILES * a.KB * 64;  // bytes: zero-points of the row block
-    const int zbytes = TILES * a.KB * 64;
+    const int zbase = rb * TILES * a.KB * 4 * a.szw;  // bytes: zero-points of the row block
+    const int zbytes = TILES * a.KB * 4 * a.szw;
     const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f};
     constexpr int STEP = 256 * 16;  // bytes per load instruction of the workgroup
     for (int off0 = threadIdx.x * 16; off0 < zbytes; off0 += 8 * STEP) {

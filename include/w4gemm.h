@@ -49,7 +49,9 @@ typedef enum {
   W4_ERR_ALIAS = -4,       /* out overlaps an input (out == residual exactly is allowed)    */
   W4_ERR_DOMAIN = -5,      /* route forced outside its T domain, or route id unknown        */
   W4_ERR_DEVICE = -6,      /* current device is not gfx950, or no device                    */
-  W4_ERR_LAUNCH = -7       /* the kernel launch failed                                       */
+  W4_ERR_LAUNCH = -7,      /* the kernel launch failed                                       */
+  W4_ERR_SCRATCH = -8      /* the allocation-free call needs more than its static scratch,
+                              or the scratch could not be located on the current device      */
 } w4_status;
 
 /* op codes for w4_route_for / w4_linear_route */
@@ -167,6 +169,22 @@ int w4_linear_add_bf16(const uint16_t* x, const void* w, const uint16_t* scales,
                        const uint16_t* zeros, const uint16_t* residual, int T, int N, int K,
                        int bits, int group, uint16_t* out, void* workspace,
                        size_t workspace_bytes, void* stream);
+
+/* ---- allocation-free bf16 linear, for callers that cannot allocate device memory (code being
+ * captured into a HIP graph, serving loops that must not call hipMalloc, harnesses that forbid
+ * it).  Same arguments, results and validation as w4_linear_bf16 without the workspace: the
+ * workspace is a static device array inside the library, W4_SCRATCH_BYTES bytes per device,
+ * held by every device the library runs on until the process ends.  Calls whose
+ * w4_bf16_workspace_bytes(T, K) exceeds W4_SCRATCH_BYTES return W4_ERR_SCRATCH.  The first
+ * call on a device locates that device's array (a host-side symbol lookup, no allocation),
+ * so make it once outside graph capture.  Every call on one device shares its array: calls
+ * that overlap on one device (concurrent streams or threads) race and must be serialised by
+ * the caller.  Nothing in the array needs to start at zero (each call writes what it reads).
+ * Calls no hipMalloc, hipFree or allocating library routine. */
+#define W4_SCRATCH_BYTES (32u << 20)
+int w4_linear_bf16_noalloc(const uint16_t* x, const void* w, const uint16_t* scales,
+                           const uint16_t* zeros, int T, int N, int K, int bits, int group,
+                           uint16_t* out, void* stream);
 
 /* ---- grouped call: several matrices that share one activation (ninfer-3080 performance notes,
  * "What changed": two parents over one activation; the projections that read one activation

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_layout_version_and_status_strings():
     assert w4.layout_version() == 1
-    for st in range(0, -8, -1):
+    for st in range(0, -9, -1):
         assert w4.status_str(st) and w4.status_str(st) != "unknown status"
     assert w4.status_str(-99) == "unknown status"
 
@@ -286,3 +286,18 @@ def test_bf16_validation(fn):
     assert _call_bf16(fn, ws=0x30000000) == -4        # over the scales
     assert _call_bf16(fn, T=0, ws=0, x=0, out=0) == 0  # T == 0 is a no-op
     assert _call_bf16(fn, group=16) == -2
+
+
+def test_noalloc_validation():
+    """The allocation-free bf16 call validates like w4_linear_bf16 and rejects, before any
+    device work, shapes whose workspace exceeds its static scratch."""
+    L = w4.lib()
+    args = (0x10000, 0x20000000, 0x30000000, 0x40000000)
+    assert L.w4_linear_bf16_noalloc(*args, 4, 256, 512, 4, 64, 0x50000000, None) == -6  # no GPU here
+    assert L.w4_linear_bf16_noalloc(*args, 4, 256, 512, 4, 16, 0x50000000, None) == -2
+    assert L.w4_linear_bf16_noalloc(*args, 0, 256, 512, 4, 64, 0, None) == 0
+    # 4096 x 6144 bf16 activations need 48 MiB of workspace: more than the 32 MiB scratch
+    assert w4.bf16_workspace_bytes(4096, 6144) > w4.SCRATCH_BYTES
+    assert L.w4_linear_bf16_noalloc(*args, 4096, 5120, 6144, 4, 64, 0x50000000, None) == -8
+    assert w4.bf16_workspace_bytes(2048, 6144) <= w4.SCRATCH_BYTES
+    assert L.w4_linear_bf16_noalloc(*args, 2048, 5120, 6144, 4, 64, 0x50000000, None) == -6

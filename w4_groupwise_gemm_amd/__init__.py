@@ -26,7 +26,9 @@ OP_LINEAR, OP_SWIGLU, OP_ADD = 0, 1, 2
 GROUP = 64
 
 _STATUS = {0: "W4_OK", -1: "W4_ERR_INVALID_ARG", -2: "W4_ERR_UNSUPPORTED", -3: "W4_ERR_MISALIGNED",
-           -4: "W4_ERR_ALIAS", -5: "W4_ERR_DOMAIN", -6: "W4_ERR_DEVICE", -7: "W4_ERR_LAUNCH"}
+           -4: "W4_ERR_ALIAS", -5: "W4_ERR_DOMAIN", -6: "W4_ERR_DEVICE", -7: "W4_ERR_LAUNCH",
+           -8: "W4_ERR_SCRATCH"}
+SCRATCH_BYTES = 32 << 20  # W4_SCRATCH_BYTES: static scratch of the allocation-free call
 
 GROUPS = (32, 64, 128)
 
@@ -35,7 +37,7 @@ EXPORTS = (
     "w4_linear_swiglu", "w4_linear_add", "w4_route_for", "w4_linear_route", "w4_route_count",
     "w4_route_name", "w4_route_domain", "w4_status_str", "w4_layout_version", "w4_linear_grouped",
     "w4_bf16_workspace_bytes", "w4_linear_bf16", "w4_linear_swiglu_bf16", "w4_linear_add_bf16",
-    "w4_linear_route_bf16",
+    "w4_linear_route_bf16", "w4_linear_bf16_noalloc",
 )
 
 
@@ -104,6 +106,8 @@ def lib() -> ctypes.CDLL:
     L.w4_linear_add_bf16.restype = i
     L.w4_linear_route_bf16.argtypes = [i, i, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, sz, vp]
     L.w4_linear_route_bf16.restype = i
+    L.w4_linear_bf16_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp]
+    L.w4_linear_bf16_noalloc.restype = i
     _lib = L
     return L
 
@@ -420,6 +424,23 @@ def linear_bf16(x, pw: PackedWeight, out=None, workspace=None, stream=None):
     """out[T, N] = x . dequant(W)^T with bf16 x and out, via ``w4_linear_bf16``.  workspace: a
     device byte tensor of >= bf16_workspace_bytes(T, K) bytes (allocated here if None)."""
     return _bf16_call(-1, OP_LINEAR, x, pw, None, out, workspace, stream)
+
+
+def linear_bf16_noalloc(x, pw: PackedWeight, out, stream=None):
+    """As linear_bf16, through ``w4_linear_bf16_noalloc``: the library's static device scratch
+    instead of a workspace (for callers that cannot allocate; `out` must be given).  Calls on
+    one device share that scratch, so they must not overlap."""
+    import torch
+    if pw.pair:
+        raise ValueError("a gate/up pair runs through linear_swiglu_bf16")
+    _check_x(x, pw.K, torch.bfloat16)
+    _check_weight(pw, x.device)
+    T = x.shape[0]
+    _check_tensor(out, "out", (T, pw.N), torch.bfloat16, x.device)
+    _check(lib().w4_linear_bf16_noalloc(_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros), T,
+                                        pw.N, pw.K, pw.bits, pw.group, _dptr(out), _stream(stream)),
+           "w4_linear_bf16_noalloc")
+    return out
 
 
 def linear_swiglu_bf16(x, pw: PackedWeight, out=None, workspace=None, stream=None):

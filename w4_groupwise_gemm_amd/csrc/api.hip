@@ -11,6 +11,7 @@
 #include <climits>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/w4gemm.h"
 #include "device.h"
@@ -362,6 +363,46 @@ extern "C" int w4_linear_add_bf16(const uint16_t* x, const void* w, const uint16
                      workspace, workspace_bytes, stream);
 }
 
+// ---- allocation-free bf16 linear: the workspace is this file's static device array.  The host
+// name `scratch` is only a stand-in for the device symbol; its device address is looked up
+// once per device (with that device current) and kept, and only that address is ever handed
+// to a kernel.
+namespace {
+__device__ __align__(256) char scratch[W4_SCRATCH_BYTES];
+
+void* g_scratch_ptr[64];
+std::mutex g_scratch_mu;
+
+int scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return W4_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return W4_ERR_SCRATCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return W4_OK;
+}
+}  // namespace
+
+extern "C" int w4_linear_bf16_noalloc(const uint16_t* x, const void* w, const uint16_t* scales,
+                                      const uint16_t* zeros, int T, int N, int K, int bits,
+                                      int group, uint16_t* out, void* stream) {
+  int st = check_shape(W4_OP_LINEAR, T, N, K, bits, group);
+  if (st != W4_OK) return st;
+  if (T == 0) return W4_OK;
+  if (bf16_ws_bytes(T, K) > (size_t)W4_SCRATCH_BYTES) return W4_ERR_SCRATCH;
+  st = device_check();
+  if (st != W4_OK) return st;
+  void* ws = nullptr;
+  st = scratch_for_current_device(&ws);
+  if (st != W4_OK) return st;
+  return run_op_bf16(-1, W4_OP_LINEAR, x, w, scales, zeros, nullptr, T, N, K, bits, group, out, ws,
+                     W4_SCRATCH_BYTES, stream);
+}
+
 extern "C" int w4_linear_route_bf16(int route_id, int op, const uint16_t* x, const void* w,
                                     const uint16_t* scales, const uint16_t* zeros,
                                     const uint16_t* residual, int T, int N, int K, int bits,
@@ -410,6 +451,7 @@ extern "C" const char* w4_status_str(int status) {
     case W4_ERR_DOMAIN: return "route unknown or T outside its domain";
     case W4_ERR_DEVICE: return "no gfx950 device current";
     case W4_ERR_LAUNCH: return "kernel launch failed";
+    case W4_ERR_SCRATCH: return "static scratch too small or not found on this device";
     default: return "unknown status";
   }
 }

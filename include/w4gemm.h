@@ -209,6 +209,25 @@ typedef struct {
 int w4_linear_grouped(const uint16_t* x, const w4_parent* parents, int nparents, int T, int K,
                       int group, void* stream);
 
+/* ---- per-verify-width graphs: launch-overhead removal for decode steps.  A decode round calls
+ * the same projections at a few token widths (concurrency x (draft + 1)); at one stream the
+ * gaps and ramp-up/drain between short kernels are a large part of the step (ninfer-3080
+ * performance notes, "What is left at C1"; Kernarc, "One decode step, top to silicon": one graph
+ * per verify width).  A set records, per width, every library call (or any other capturable
+ * work) the caller enqueues on `stream` between w4_graph_set_begin and w4_graph_set_end, and
+ * w4_graph_set_launch replays that width's instantiated graph in one launch.  The buffers the
+ * recorded calls name must stay allocated at the same addresses while the graph is replayed;
+ * their contents are read at replay time.  One capture at a time per set; a width is recorded
+ * once (begin on a recorded width is W4_ERR_INVALID_ARG).  The set allocates host memory only.
+ * stream must not be NULL (the null stream cannot be captured). */
+typedef struct w4_graph_set w4_graph_set;
+w4_graph_set* w4_graph_set_create(void);  /* NULL if out of host memory */
+int w4_graph_set_begin(w4_graph_set* set, int width, void* stream);  /* starts stream capture */
+int w4_graph_set_end(w4_graph_set* set, int width, void* stream);    /* ends it, instantiates */
+int w4_graph_set_launch(w4_graph_set* set, int width, void* stream); /* W4_ERR_DOMAIN: not recorded */
+int w4_graph_set_has(w4_graph_set* set, int width);                  /* 1 if recorded, else 0 */
+void w4_graph_set_destroy(w4_graph_set* set);
+
 /* ---- routes: every op has several kernels ("schedules"), each with an explicit T domain
  * (ninfer-3080 performance notes, "Route boundaries are measured here").  The three calls
  * above pick exactly one route with w4_route_for and launch it once. */

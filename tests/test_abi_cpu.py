@@ -301,3 +301,18 @@ def test_noalloc_validation():
     assert L.w4_linear_bf16_noalloc(*args, 4096, 5120, 6144, 4, 64, 0x50000000, None) == -8
     assert w4.bf16_workspace_bytes(2048, 6144) <= w4.SCRATCH_BYTES
     assert L.w4_linear_bf16_noalloc(*args, 2048, 5120, 6144, 4, 64, 0x50000000, None) == -6
+
+
+def test_graph_set_host_side():
+    """Graph sets: creation, lookups and misuse are answered on the host (no GPU here)."""
+    L = w4.lib()
+    g = L.w4_graph_set_create()
+    assert g
+    assert L.w4_graph_set_has(g, 4) == 0
+    assert L.w4_graph_set_launch(g, 4, None) == -5            # nothing recorded for width 4
+    assert L.w4_graph_set_begin(g, 4, None) == -1             # the null stream cannot be captured
+    assert L.w4_graph_set_begin(None, 4, 0x1234) == -1
+    assert L.w4_graph_set_begin(g, -1, 0x1234) == -1
+    assert L.w4_graph_set_end(g, 4, 0x1234) == -1             # no capture in progress
+    L.w4_graph_set_destroy(g)
+    L.w4_graph_set_destroy(None)

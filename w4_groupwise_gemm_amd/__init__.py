@@ -37,7 +37,8 @@ EXPORTS = (
     "w4_linear_swiglu", "w4_linear_add", "w4_route_for", "w4_linear_route", "w4_route_count",
     "w4_route_name", "w4_route_domain", "w4_status_str", "w4_layout_version", "w4_linear_grouped",
     "w4_bf16_workspace_bytes", "w4_linear_bf16", "w4_linear_swiglu_bf16", "w4_linear_add_bf16",
-    "w4_linear_route_bf16", "w4_linear_bf16_noalloc",
+    "w4_linear_route_bf16", "w4_linear_bf16_noalloc", "w4_graph_set_create", "w4_graph_set_begin",
+    "w4_graph_set_end", "w4_graph_set_launch", "w4_graph_set_has", "w4_graph_set_destroy",
 )
 
 
@@ -108,6 +109,15 @@ def lib() -> ctypes.CDLL:
     L.w4_linear_route_bf16.restype = i
     L.w4_linear_bf16_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp]
     L.w4_linear_bf16_noalloc.restype = i
+    L.w4_graph_set_create.argtypes = []
+    L.w4_graph_set_create.restype = vp
+    for name in ("w4_graph_set_begin", "w4_graph_set_end", "w4_graph_set_launch"):
+        getattr(L, name).argtypes = [vp, i, vp]
+        getattr(L, name).restype = i
+    L.w4_graph_set_has.argtypes = [vp, i]
+    L.w4_graph_set_has.restype = i
+    L.w4_graph_set_destroy.argtypes = [vp]
+    L.w4_graph_set_destroy.restype = None
     _lib = L
     return L
 
@@ -457,6 +467,63 @@ def linear_route_bf16(route_id: int, op: int, x, pw: PackedWeight, residual=None
     if route_id < 0:
         raise ValueError("route id must be >= 0")
     return _bf16_call(route_id, op, x, pw, residual, out, workspace, stream)
+
+
+# ------------------------------------------------------------------ per-verify-width graphs
+
+class VerifyGraphs:
+    """One recorded graph per token width, over ``w4_graph_set_*``.
+
+    ``run(T, step)``: the first time a width is seen, ``step(T)`` is called once with the
+    stream captured (it enqueues that width's library calls on ``stream``: every call of this
+    library is capturable), and the instantiated graph is kept; every call then replays it in
+    one launch.  The tensors ``step`` uses must outlive the set and keep their addresses; their
+    contents are read at replay time.  The stream must not be the null stream."""
+
+    def __init__(self, stream=None):
+        import torch
+        self._stream = torch.cuda.Stream() if stream is None else stream
+        self._set = lib().w4_graph_set_create()
+        if not self._set:
+            raise MemoryError("w4_graph_set_create")
+
+    @property
+    def stream(self):
+        return self._stream
+
+    def recorded(self, T: int) -> bool:
+        return bool(lib().w4_graph_set_has(self._set, T))
+
+    def record(self, T: int, step) -> None:
+        import torch
+        h = self._stream.cuda_stream
+        torch.cuda.current_stream().synchronize()
+        with torch.cuda.stream(self._stream):
+            _check(lib().w4_graph_set_begin(self._set, T, h), "w4_graph_set_begin")
+            try:
+                step(T)
+            finally:
+                st = lib().w4_graph_set_end(self._set, T, h)
+            _check(st, "w4_graph_set_end")
+
+    def run(self, T: int, step=None) -> None:
+        """Replay the width-T graph on the set's stream (recording it first if needed)."""
+        if not self.recorded(T):
+            if step is None:
+                raise KeyError(f"no graph recorded for width {T}")
+            self.record(T, step)
+        _check(lib().w4_graph_set_launch(self._set, T, self._stream.cuda_stream), "w4_graph_set_launch")
+
+    def close(self) -> None:
+        if self._set:
+            lib().w4_graph_set_destroy(self._set)
+            self._set = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # pragma: no cover -- interpreter shutdown
+            pass
 
 
 def route_for(op: int, bits: int, T: int, N: int, K: int) -> int:

@@ -112,6 +112,11 @@ def main() -> int:
                     help="read probe over rotated copies (--cold-bytes GiB), graph-replayed "
                          "back to back like the GEMM launches: the cold-read ceiling at that size")
     ap.add_argument("--probe-grid", type=int, default=2048, help="workgroups of the probe kernels")
+    ap.add_argument("--probe-unroll", type=int, default=1, choices=[1, 2, 4, 8],
+                    help="independent 16-byte loads in flight per lane in the read probe")
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="with --probe read --probe-cold: sweep unroll 1/2/4/8 x grid 256..16384 and "
+                         "report the fastest (the cold-read ceiling at --probe-mb)")
     ap.add_argument("--widths", default=None,
                     help="comma list of T overriding the workload's widths (counter runs)")
     ap.add_argument("--no-graph", action="store_true",
@@ -550,6 +555,8 @@ def run_probe(args) -> int:
     P = ctypes.CDLL(os.path.join(ROOT, "w4_groupwise_gemm_amd", "libw4probe.so"))
     P.w4probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     P.w4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    P.w4probe_read_u.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
     nbytes = int(args.probe_mb * 1e6) // 4096 * 4096
     dev = torch.device("cuda:0")
     grid = args.probe_grid
@@ -562,30 +569,46 @@ def run_probe(args) -> int:
         bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(copies)]
         sink = torch.empty(16, dtype=torch.uint8, device=dev)
 
-        def launch_all():
-            cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)  # the capture stream
-            for b in bufs:
-                if P.w4probe_read(b.data_ptr(), nbytes, sink.data_ptr(), grid, cs) != 0:
-                    raise RuntimeError("probe launch failed")
+        def measure(g_wg, unroll):
+            def launch_all():
+                cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)  # the capture stream
+                for b in bufs:
+                    if P.w4probe_read_u(b.data_ptr(), nbytes, sink.data_ptr(), g_wg, unroll, cs) != 0:
+                        raise RuntimeError("probe launch failed")
 
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            launch_all()
-        stream = torch.cuda.current_stream()
-        for _ in range(max(1, args.warmup)):
-            g.replay()
-        torch.cuda.synchronize()
-        samples = []
-        for _ in range(max(1, args.steps)):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                launch_all()
+            stream = torch.cuda.current_stream()
+            for _ in range(max(1, args.warmup)):
+                g.replay()
             torch.cuda.synchronize()
-            samples.append(e0.elapsed_time(e1) * 1e3 / copies)
-        us = float(np.median(samples))
+            samples = []
+            for _ in range(max(1, args.steps)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                samples.append(e0.elapsed_time(e1) * 1e3 / copies)
+            return float(np.median(samples))
+
+        if args.probe_sweep:
+            table = {}
+            for unroll in (1, 2, 4, 8):
+                for g_wg in (256, 512, 1024, 2048, 4096, 8192, 16384):
+                    us = measure(g_wg, unroll)
+                    table[f"u{unroll}_g{g_wg}"] = us
+                    print(f"[probe] {nbytes / 1e6:.1f} MB unroll={unroll} grid={g_wg}: {us:.2f} us "
+                          f"{nbytes / us / 1e3:.0f} GB/s", file=sys.stderr, flush=True)
+            best = min(table, key=table.get)
+            print(json.dumps({"probe": "read_cold_sweep", "bytes_read": nbytes, "copies": copies,
+                              "us": table, "best": best, "best_us": table[best],
+                              "best_GBs": nbytes / table[best] / 1e3}))
+            return 0
+        us = measure(grid, args.probe_unroll)
         print(json.dumps({"probe": "read_cold", "bytes_read": nbytes, "copies": copies, "grid": grid,
-                          "us_median": us, "GBs": nbytes / us / 1e3}))
+                          "unroll": args.probe_unroll, "us_median": us, "GBs": nbytes / us / 1e3}))
         return 0
     src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dst = torch.empty(nbytes if args.probe == "copy" else 16, dtype=torch.uint8, device=dev)

@@ -21,5 +21,7 @@ from .reference import (  # noqa: F401
     linear_add,
     fp16_round,
     bf16_value,
+    quantize_a8,
+    linear_a8,
     rel_l2,
 )

@@ -139,6 +139,40 @@ def linear_add(x, lo, hi, scales, zeros, r, bits: int, group: int = GROUP) -> np
     return linear(x, lo, hi, scales, zeros, bits, group) + np.asarray(r).astype(np.float64)
 
 
+A8_GROUP = 64
+
+
+def quantize_a8(x: np.ndarray, group: int = A8_GROUP):
+    """Per-(token, group) symmetric int8 activations of the A8 prefill route.
+
+    The ninfer-3080 performance notes ("A8 prefill routes", and the quality paragraph of
+    "cuBLAS prefill route") quantise the activations to int8 with a scale per 64 columns and
+    hold the result to a relative L2 error of 0.04 against an fp64 oracle; they give no formula.
+    Reading: per token row and 64-column group, m = max |x|, scale s = m / 127 and code
+    q = rint(x / s) (round half to even) clamped to [-127, 127], both divisions in fp32; a
+    group of zeros has s = 0 and q = 0.  Returns (q int8 [T, K], s float32 [T, K / group])."""
+    x32 = np.asarray(x).astype(np.float32)
+    T, K = x32.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    xg = x32.reshape(T, K // group, group)
+    m = np.max(np.abs(xg), axis=2)
+    s = (m / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+    q = np.rint(xg / safe[:, :, None])
+    q = np.where(s[:, :, None] > 0, q, 0.0)
+    q = np.clip(q, -127, 127).astype(np.int8)
+    return q.reshape(T, K), s
+
+
+def linear_a8(x, lo, hi, scales, zeros, bits: int, group: int = GROUP) -> np.ndarray:
+    """The A8 route's product in fp64: Y = Xa . dequant(W)^T with Xa[t, k] = s[t, g] * q[t, k]
+    the int8 activations of quantize_a8 (groups of 64 columns)."""
+    q, s = quantize_a8(x)
+    xa = q.astype(np.float64) * np.repeat(s.astype(np.float64), A8_GROUP, axis=1)
+    return linear(xa, lo, hi, scales, zeros, bits, group)
+
+
 def bf16_value(bits: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns (uint16) -> their exact values in fp64.
 

@@ -399,6 +399,59 @@ def test_generator_bf16_rounding():
     assert np.array_equal(bf16_bits(oracle.bf16_value(allb).astype(np.float32)), allb)
 
 
+def test_quantize_a8_hand_values():
+    """A group whose largest magnitude is 127 has scale exactly 1, so the codes are the
+    activations rounded half to even; other values are worked out by hand."""
+    x = np.zeros((2, 64), dtype=np.float16)
+    x[0, :8] = [127, 0.5, 1.5, 2.5, -0.5, -1.5, 126.5, -3.25]
+    x[1, :3] = [2.5, -1.0, 0.25]          # m = 2.5: s = fp32(2.5 / 127)
+    q, s = oracle.quantize_a8(x)
+    assert s[0, 0] == np.float32(1.0)
+    assert list(q[0, :8]) == [127, 0, 2, 2, 0, -2, 126, -3]
+    assert s[1, 0] == np.float32(2.5) / np.float32(127.0)
+    # -1 / (2.5 / 127) = -50.8 -> -51;  0.25 / (2.5 / 127) = 12.7 -> 13
+    assert list(q[1, :3]) == [127, -51, 13]
+    assert np.all(q[:, 8:64][0] == 0) and np.all(q[1, 3:] == 0)
+
+
+def test_quantize_a8_properties():
+    """Zero groups give zero scale and codes; every nonzero group reaches |q| = 127; the
+    reconstruction error is at most half a step; groups are independent."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((5, 256)) * 2).astype(np.float16)
+    x[1, 64:128] = 0
+    x[:, 7] *= np.float16(30)
+    q, s = oracle.quantize_a8(x)
+    assert s[1, 1] == 0 and np.all(q[1, 64:128] == 0)
+    for t in range(5):
+        for g in range(4):
+            if s[t, g] > 0:
+                assert np.max(np.abs(q[t, 64 * g:64 * (g + 1)].astype(int))) == 127
+    err = np.abs(x.astype(np.float64) - q * np.repeat(s.astype(np.float64), 64, axis=1))
+    assert np.all(err <= np.repeat(s.astype(np.float64), 64, axis=1) * (0.5 + 1e-6))
+    x2 = x.copy()
+    x2[:, 64:128] *= np.float16(4)
+    q2, s2 = oracle.quantize_a8(x2)
+    assert np.array_equal(q2[:, :64], q[:, :64]) and np.array_equal(s2[:, [0, 2, 3]], s[:, [0, 2, 3]])
+
+
+def test_linear_a8_exact_case_and_accuracy_bar():
+    """Integer activations whose groups reach 127 are carried exactly (scale 1), so the A8
+    product equals the exact one; on the prefill workload's inputs (N(0, 1) with 8 channels
+    x30) the A8 product is within the pages' 0.04 relative L2 allowance of the exact one."""
+    rng = np.random.default_rng(4)
+    q, lo, hi, s, z, x = _tiny_case(rng, 8, 256, 3, 5)
+    xi = rng.integers(-127, 128, size=(3, 256)).astype(np.float16)
+    xi[:, ::64] = 127
+    assert np.array_equal(ref.linear_a8(xi, lo, hi, s, z, 5), ref.linear(xi, lo, hi, s, z, 5))
+    from synth import make_weights, make_activations
+    w = make_weights(rng, "w", 256, 1024, 5, ("const", 16), (0.0025, 0.01))
+    xa, _ = make_activations(rng, 64, 1024, 1.0, 8)
+    exact = ref.linear(xa, w.lo, w.hi, w.scales, w.zeros, 5)
+    rel = oracle.rel_l2(ref.linear_a8(xa, w.lo, w.hi, w.scales, w.zeros, 5), exact)
+    assert 1e-3 < rel <= 0.04, rel
+
+
 def test_rel_l2_and_round():
     assert oracle.rel_l2(np.array([1.0, 0.0]), np.array([1.0, 0.0])) == 0.0
     assert abs(oracle.rel_l2(np.array([3.0, 4.0]), np.array([0.0, 5.0])) - np.sqrt(10.0) / 5.0) < 1e-15

@@ -358,6 +358,11 @@ def run_workload(args, wname, torch, w4, cpu_timing):
                                    ze if not pair else None, wstream_alg, prefill, rows, K, gpu_out,
                                    timing=cpu_timing)
         print(f"[bench] {wname} parity {parity}", file=sys.stderr, flush=True)
+        if context and "a8_route" in context:
+            a8_accuracy(wl, context["a8_route"], bits, op)
+    if context and "a8_route" in context:
+        for d in context["a8_route"]["per_T"].values():
+            d.pop("_sample", None)
     parity_ok = None if parity is None else all(p["ok"] for p in parity.values())
 
     line = {
@@ -461,7 +466,61 @@ def context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, de
         del wkn, wnk
         out["dense_fp16_gemm_ceiling"] = {"what": "vendor-library fp16 GEMM (torch.matmul / linear) on random "
                                                   "fp16 weights of the same shape, cold copies", "per_T": dense}
+        if op in (w4.OP_ADD, w4.OP_LINEAR) and bits in (4, 5):
+            out["a8_route"] = a8_route(w4, torch, args, timed, wl, widths, bits, K, N, op, dev)
     return out or None
+
+
+def a8_route(w4, torch, args, timed, wl, widths, bits, K, N, op, dev):
+    """The lossy A8 route on the same workload (int8 activations per 64 columns): per width the
+    time of the whole call (quantisation + GEMM), of the quantisation alone and of the GEMM on
+    pre-quantised activations, over rotated cold weight copies; effective rate 2 T N K / time.
+    Its accuracy against the exact product is added by the oracle leg (a8_accuracy)."""
+    ws0 = wl.weights[0]
+    packed = w4.repack(ws0.lo, ws0.hi, ws0.scales, ws0.zeros, bits)
+    nbytes = sum(int(a.nbytes) for a in packed)
+    copies = max(2, int(np.ceil(args.cold_bytes * (1 << 30) / nbytes)))
+    pws = [w4.to_device(packed, N, K, bits, False, device=dev) for _ in range(copies)]
+    res = {}
+    for T in widths:
+        x = torch.from_numpy(np.ascontiguousarray(wl.x[:T])).to(dev)
+        r = torch.from_numpy(np.ascontiguousarray(wl.r[:T])).to(dev) if wl.r is not None else None
+        y = torch.empty((T, N), dtype=torch.float16, device=dev)
+        ws = torch.empty(w4.a8_workspace_bytes(T, K), dtype=torch.uint8, device=dev)
+
+        def call(c, xx=x):
+            if op == w4.OP_ADD:
+                w4.linear_add_a8(xx, pws[c], r, out=y, workspace=ws, T=T)
+            else:
+                w4.linear_a8(xx, pws[c], out=y, workspace=ws, T=T)
+        us_all = timed(lambda c: call(c), copies)
+        us_q = timed(lambda c: w4.quantize_a8(x, workspace=ws), copies)
+        w4.quantize_a8(x, workspace=ws)
+        us_gemm = timed(lambda c: call(c, None), copies)
+        call(0)
+        torch.cuda.synchronize()
+        cols = np.sort(np.random.default_rng(T).choice(N, 256, replace=False))
+        res[str(T)] = {"us": us_all, "us_quantise": us_q, "us_gemm": us_gemm,
+                       "TOPs": 2.0 * T * N * K / (us_all * 1e6),
+                       "_sample": (cols, y.cpu().numpy().astype(np.float64)[:, cols])}
+    del pws
+    return {"what": "lossy A8 route: int8 activations with a scale per 64 columns, int8 matrix-core "
+                    "steps, per-group rescale (w4_linear*_a8); cold weight copies", "per_T": res}
+
+
+def a8_accuracy(wl, ctx, bits, op):
+    """Oracle leg: relative L2 error of the A8 route's sampled outputs against the exact fp64
+    product (the pages hold the route to 0.04)."""
+    import oracle
+    ws0 = wl.weights[0]
+    for T, d in ctx["per_T"].items():
+        cols, got = d.pop("_sample")
+        T = int(T)
+        ref = oracle.linear_rows(wl.x[:T], ws0.lo, ws0.hi, ws0.scales, ws0.zeros, bits, cols)
+        if op == 2:
+            ref = ref + wl.r[:T][:, cols].astype(np.float64)
+        d["rel_l2_vs_exact"] = oracle.rel_l2(got, ref)
+        d["within_0.04"] = bool(d["rel_l2_vs_exact"] <= 0.04)
 
 
 def mixed_bits_parents(w4, torch, args, timed, K, dev):

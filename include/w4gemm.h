@@ -170,6 +170,35 @@ int w4_linear_add_bf16(const uint16_t* x, const void* w, const uint16_t* scales,
                        int bits, int group, uint16_t* out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* ---- A8 prefill route (lossy): int8 activations with a scale per 64 columns, int8 matrix-core
+ * steps, the int32 partial sum of each 64-column group rescaled into fp32 (ninfer-3080
+ * performance notes, "A8 prefill routes": per-group activation quantisation, held to a
+ * relative L2 error of 0.04 against an fp64 oracle).  Per token row t and 64-column group g:
+ * s[t][g] = max |x| / 127 and q[t][k] = rint(x[t][k] / s[t][g]) clamped to [-127, 127], both in
+ * fp32 (a group of zeros: s = 0, q = 0); the call returns fp16(sum_k s q W^T) with the same
+ * epilogues as the fp16 ops.  Requirements beyond the fp16 ops: group == 64 (else
+ * W4_ERR_UNSUPPORTED) and integer zero-points in [0, 127] (any other zero-point turns the outputs
+ * of the 128-row block that holds it into NaN).
+ * workspace: caller-owned device memory of at least w4_a8_workspace_bytes(T, K) bytes, 16-byte
+ * aligned, overlapping no argument.  Its layout: int8 codes [T][K] at offset 0, each 8-column run
+ * stored as columns 0 4 1 5 2 6 3 7; fp32 scales at offset ceil16(T * K), as
+ * [ceil(K / 128)][T][2] (group g of token t at [g / 2][t][g % 2]).
+ * x may be NULL in the three ops: the workspace then already holds this T x K activation, as
+ * written by w4_quantize_a8 (matrices that read one activation quantise it once).  Each op
+ * enqueues the quantisation (unless x is NULL) and one GEMM kernel. */
+size_t w4_a8_workspace_bytes(int T, int K); /* 0 if the shape is invalid */
+int w4_quantize_a8(const uint16_t* x, int T, int K, void* workspace, size_t workspace_bytes,
+                   void* stream);
+int w4_linear_a8(const uint16_t* x, const void* w, const uint16_t* scales, const uint16_t* zeros,
+                 int T, int N, int K, int bits, int group, uint16_t* out, void* workspace,
+                 size_t workspace_bytes, void* stream);
+int w4_linear_swiglu_a8(const uint16_t* x, const void* w_pair, const uint16_t* scales_pair,
+                        const uint16_t* zeros_pair, int T, int N, int K, int bits, int group,
+                        uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+int w4_linear_add_a8(const uint16_t* x, const void* w, const uint16_t* scales, const uint16_t* zeros,
+                     const uint16_t* residual, int T, int N, int K, int bits, int group,
+                     uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- allocation-free bf16 linear, for callers that cannot allocate device memory (code being
  * captured into a HIP graph, serving loops that must not call hipMalloc, harnesses that forbid
  * it).  Same arguments, results and validation as w4_linear_bf16 without the workspace: the

@@ -316,3 +316,25 @@ def test_graph_set_host_side():
     assert L.w4_graph_set_end(g, 4, 0x1234) == -1             # no capture in progress
     L.w4_graph_set_destroy(g)
     L.w4_graph_set_destroy(None)
+
+
+def test_a8_validation():
+    """A8 calls: workspace size and placement, group 64 only, validation before device work."""
+    L = w4.lib()
+    T, N, K = 4, 256, 512
+    nb = w4.a8_workspace_bytes(T, K)
+    assert nb == 4 * 512 + 4 * 4 * 2 * 4 and w4.a8_workspace_bytes(1, 100) == 0
+    x, w, s, z, out, ws = 0x10000, 0x20000000, 0x30000000, 0x40000000, 0x50000000, 0x70000000
+    assert L.w4_linear_a8(x, w, s, z, T, N, K, 4, 64, out, ws, nb, None) == -6      # valid: no GPU here
+    assert L.w4_linear_a8(0, w, s, z, T, N, K, 4, 64, out, ws, nb, None) == -6      # pre-quantised
+    assert L.w4_linear_a8(x, w, s, z, T, N, K, 4, 32, out, ws, nb, None) == -2      # group 64 only
+    assert L.w4_linear_a8(x, w, s, z, T, N, K, 4, 16, out, ws, nb, None) == -2
+    assert L.w4_linear_a8(x, w, s, z, T, N, K, 4, 64, out, ws, nb - 1, None) == -1  # short workspace
+    assert L.w4_linear_a8(x, w, s, z, T, N, K, 4, 64, out, 0, nb, None) == -1
+    assert L.w4_linear_a8(x, w, s, z, T, N, K, 4, 64, out, ws + 8, nb, None) == -3
+    assert L.w4_linear_a8(x, w, s, z, T, N, K, 4, 64, out, out - 64, nb, None) == -4  # over out
+    assert L.w4_linear_add_a8(x, w, s, z, 0x60000000, T, N, K, 5, 64, out, 0x60000000 - 16, nb, None) == -4
+    assert L.w4_linear_a8(x, w, s, z, 0, N, K, 4, 64, 0, 0, 0, None) == 0           # T == 0
+    assert L.w4_quantize_a8(x, T, K, ws, nb, None) == -6
+    assert L.w4_quantize_a8(x, T, K, x + 64, nb, None) == -4
+    assert L.w4_quantize_a8(x, T, 100, ws, nb, None) == -1

@@ -39,6 +39,7 @@ EXPORTS = (
     "w4_bf16_workspace_bytes", "w4_linear_bf16", "w4_linear_swiglu_bf16", "w4_linear_add_bf16",
     "w4_linear_route_bf16", "w4_linear_bf16_noalloc", "w4_graph_set_create", "w4_graph_set_begin",
     "w4_graph_set_end", "w4_graph_set_launch", "w4_graph_set_has", "w4_graph_set_destroy",
+    "w4_a8_workspace_bytes", "w4_quantize_a8", "w4_linear_a8", "w4_linear_swiglu_a8", "w4_linear_add_a8",
 )
 
 
@@ -118,6 +119,16 @@ def lib() -> ctypes.CDLL:
     L.w4_graph_set_has.restype = i
     L.w4_graph_set_destroy.argtypes = [vp]
     L.w4_graph_set_destroy.restype = None
+    L.w4_a8_workspace_bytes.argtypes = [i, i]
+    L.w4_a8_workspace_bytes.restype = sz
+    L.w4_quantize_a8.argtypes = [vp, i, i, vp, sz, vp]
+    L.w4_quantize_a8.restype = i
+    L.w4_linear_a8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, sz, vp]
+    L.w4_linear_a8.restype = i
+    L.w4_linear_swiglu_a8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, sz, vp]
+    L.w4_linear_swiglu_a8.restype = i
+    L.w4_linear_add_a8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, sz, vp]
+    L.w4_linear_add_a8.restype = i
     _lib = L
     return L
 
@@ -467,6 +478,85 @@ def linear_route_bf16(route_id: int, op: int, x, pw: PackedWeight, residual=None
     if route_id < 0:
         raise ValueError("route id must be >= 0")
     return _bf16_call(route_id, op, x, pw, residual, out, workspace, stream)
+
+
+# ------------------------------------------------------------------ A8 prefill route (lossy)
+
+def a8_workspace_bytes(T: int, K: int) -> int:
+    return int(lib().w4_a8_workspace_bytes(T, K))
+
+
+def _a8_workspace(workspace, T: int, K: int, device):
+    import torch
+    nbytes = a8_workspace_bytes(T, K)
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device or \
+            not workspace.is_contiguous() or workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must be a contiguous tensor of >= {nbytes} bytes on {device}")
+    return workspace
+
+
+def quantize_a8(x, workspace=None, stream=None):
+    """Quantise x (fp16 [T, K]) into the A8 workspace (int8 codes + scales per 64 columns); the
+    workspace can then serve several A8 calls with x=None."""
+    _check_x(x, x.shape[1] if x.dim() == 2 else -1)
+    T, K = x.shape
+    ws = _a8_workspace(workspace, T, K, x.device)
+    _check(lib().w4_quantize_a8(_dptr(x), T, K, _dptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "w4_quantize_a8")
+    return ws
+
+
+def _a8_call(op: int, x, pw: PackedWeight, residual, out, workspace, stream, T=None):
+    """x: fp16 [T, K], or None with a workspace that quantize_a8 filled (then T is given)."""
+    import torch
+    if (op == OP_SWIGLU) != pw.pair:
+        raise ValueError("the SwiGLU op takes a gate/up pair from pack_pair; the others a single matrix")
+    if x is not None:
+        _check_x(x, pw.K)
+        T, dev = x.shape[0], x.device
+    else:
+        if workspace is None or T is None:
+            raise ValueError("without x, give the quantised workspace and T")
+        dev = workspace.device
+    _check_weight(pw, dev)
+    like = torch.empty(0, dtype=torch.float16, device=dev)
+    if op == OP_ADD:
+        _check_tensor(residual, "residual", (T, pw.N), torch.float16, dev)
+    else:
+        residual = None
+    if out is None:
+        out = torch.empty((T, pw.N), dtype=torch.float16, device=dev)
+    _check_tensor(out, "out", (T, pw.N), like.dtype, dev)
+    ws = _a8_workspace(workspace, T, pw.K, dev)
+    nb = ws.numel() * ws.element_size()
+    args = (_dptr(x), _dptr(pw.w), _dptr(pw.scales), _dptr(pw.zeros))
+    L = lib()
+    if op == OP_SWIGLU:
+        st = L.w4_linear_swiglu_a8(*args, T, pw.N, pw.K, pw.bits, pw.group, _dptr(out), _dptr(ws), nb,
+                                   _stream(stream))
+    elif op == OP_ADD:
+        st = L.w4_linear_add_a8(*args, _dptr(residual), T, pw.N, pw.K, pw.bits, pw.group, _dptr(out),
+                                _dptr(ws), nb, _stream(stream))
+    else:
+        st = L.w4_linear_a8(*args, T, pw.N, pw.K, pw.bits, pw.group, _dptr(out), _dptr(ws), nb,
+                            _stream(stream))
+    _check(st, "w4_linear*_a8")
+    return out
+
+
+def linear_a8(x, pw: PackedWeight, out=None, workspace=None, stream=None, T=None):
+    """A8 route (lossy, int8 activations per 64 columns): out = x . dequant(W)^T."""
+    return _a8_call(OP_LINEAR, x, pw, None, out, workspace, stream, T)
+
+
+def linear_swiglu_a8(x, pw: PackedWeight, out=None, workspace=None, stream=None, T=None):
+    return _a8_call(OP_SWIGLU, x, pw, None, out, workspace, stream, T)
+
+
+def linear_add_a8(x, pw: PackedWeight, residual, out=None, workspace=None, stream=None, T=None):
+    return _a8_call(OP_ADD, x, pw, residual, out, workspace, stream, T)
 
 
 # ------------------------------------------------------------------ per-verify-width graphs

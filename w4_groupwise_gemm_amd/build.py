@@ -21,7 +21,7 @@ PROBE_LIB = os.path.join(HERE, "libw4probe.so")  # measurement support (read/cop
 # (source, extra defines, object) -- stream.hip is compiled once per code width and epilogue
 STREAM_PARTS = [("stream.hip", [f"-DW4_STREAM_BITS={b}", f"-DW4_STREAM_EPI={e}"], f"stream_b{b}_e{e}.o")
                 for b in (4, 5) for e in (0, 1, 2)]
-SOURCES = STREAM_PARTS + ["api.hip", "narrow.hip", "splitk.hip", "wide.hip", "bf16.hip", "repack.cpp", "graphs.cpp"]
+SOURCES = STREAM_PARTS + ["api.hip", "narrow.hip", "splitk.hip", "wide.hip", "bf16.hip", "a8.hip", "repack.cpp", "graphs.cpp"]
 PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")

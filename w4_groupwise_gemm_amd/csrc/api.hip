@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <initializer_list>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -74,12 +75,13 @@ struct Range {
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// x_optional: x may be NULL (the A8 calls with pre-quantised activations); it is then not checked.
 int validate(int op, const void* x, const void* w, const void* s, const void* z, const void* res,
-             int T, int N, int K, int bits, int group, const void* out) {
+             int T, int N, int K, int bits, int group, const void* out, bool x_optional = false) {
   int st = check_shape(op, T, N, K, bits, group);
   if (st != W4_OK) return st;
   if (T == 0) return W4_OK;
-  if (!x || !w || !s || !z || !out) return W4_ERR_INVALID_ARG;
+  if ((!x && !x_optional) || !w || !s || !z || !out) return W4_ERR_INVALID_ARG;
   if (op == W4_OP_ADD && !res) return W4_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w) || !aligned16(s) || !aligned16(z) || !aligned16(out))
     return W4_ERR_MISALIGNED;
@@ -96,7 +98,7 @@ int validate(int op, const void* x, const void* w, const void* s, const void* z,
   if ((size_t)T * K * 2 >= kLimit || (size_t)T * N * 2 >= kLimit || wbytes >= kLimit)
     return W4_ERR_UNSUPPORTED;
   const Range ro = rng(out, (size_t)T * N * 2);
-  if (overlap(ro, rng(x, (size_t)T * K * 2)) || overlap(ro, rng(w, wbytes)) ||
+  if ((x && overlap(ro, rng(x, (size_t)T * K * 2))) || overlap(ro, rng(w, wbytes)) ||
       overlap(ro, rng(s, szbytes)) || overlap(ro, rng(z, szbytes)))
     return W4_ERR_ALIAS;
   if (op == W4_OP_ADD && res != out && overlap(ro, rng(res, (size_t)T * N * 2)))
@@ -333,6 +335,113 @@ extern "C" int w4_linear_grouped(const uint16_t* x, const w4_parent* parents, in
     if (e != W4_OK) return e;
   }
   return W4_OK;
+}
+
+// ---- A8 route: int8 activations (scale per 64 columns), int8 matrix-core GEMM
+size_t a8_ws_bytes(int T, int K) {
+  return align16((size_t)T * K) + (size_t)w4layout::num_kblocks(K) * T * 2 * sizeof(float);
+}
+
+// Workspace checks shared by the A8 calls: present, aligned, large enough, overlapping none of
+// the given ranges.
+int check_a8_ws(const void* ws, size_t ws_bytes, int T, int K, std::initializer_list<Range> others) {
+  if (!ws) return W4_ERR_INVALID_ARG;
+  if (!aligned16(ws)) return W4_ERR_MISALIGNED;
+  const size_t need = a8_ws_bytes(T, K);
+  if (ws_bytes < need) return W4_ERR_INVALID_ARG;
+  const uintptr_t b = reinterpret_cast<uintptr_t>(ws);
+  for (const Range& r : others)
+    if (overlap(Range{b, b + need}, r)) return W4_ERR_ALIAS;
+  return W4_OK;
+}
+
+Range span(const void* p, size_t n) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(p);
+  return Range{b, b + (p ? n : 0)};
+}
+
+int run_a8(int op, const void* x, const void* w, const void* s, const void* z, const void* res, int T,
+           int N, int K, int bits, int group, void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (group != 64) return check_shape(op, T, N, K, bits, group) == W4_OK ? W4_ERR_UNSUPPORTED
+                                                                          : check_shape(op, T, N, K, bits, group);
+  // x may be NULL: the workspace then already holds this T x K activation, quantised by
+  // w4_quantize_a8
+  int st = validate(op, x, w, s, z, res, T, N, K, bits, group, out, /*x_optional=*/true);
+  if (st != W4_OK) return st;
+  if (T == 0) return W4_OK;
+  const int rows = op == W4_OP_SWIGLU ? 2 * N : N;
+  st = check_a8_ws(ws, ws_bytes, T, K,
+                   {span(x, (size_t)T * K * 2), span(out, (size_t)T * N * 2),
+                    span(w, w4_packed_bytes(rows, K, bits, group)), span(s, w4_packed_sz_bytes(rows, K, group)),
+                    span(z, w4_packed_sz_bytes(rows, K, group)),
+                    span(op == W4_OP_ADD ? res : nullptr, (size_t)T * N * 2)});
+  if (st != W4_OK) return st;
+  st = device_check();
+  if (st != W4_OK) return st;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  int8_t* xq = static_cast<int8_t*>(ws);
+  float* sx = reinterpret_cast<float*>(static_cast<char*>(ws) + align16((size_t)T * K));
+  if (x && w4::launch_a8_quant(static_cast<const _Float16*>(x), T, K, xq, sx, hs) != hipSuccess)
+    return W4_ERR_LAUNCH;
+  w4::KArgs a;
+  a.x = reinterpret_cast<const _Float16*>(xq);
+  a.w = static_cast<const uint8_t*>(w);
+  a.sc = static_cast<const uint32_t*>(s);
+  a.zr = static_cast<const uint32_t*>(z);
+  a.res = op == W4_OP_ADD ? static_cast<const _Float16*>(res) : nullptr;
+  a.out = static_cast<_Float16*>(out);
+  a.T = T;
+  a.rows = rows;
+  a.K = K;
+  a.KB = w4layout::num_kblocks(K);
+  a.ldo = N;
+  a.szw = w4layout::sz_words(group);
+  a.xexp = nullptr;
+  const int epi = op == W4_OP_SWIGLU ? w4dev::EPI_SWIGLU : op == W4_OP_ADD ? w4dev::EPI_ADD : w4dev::EPI_STORE;
+  return w4::launch_a8(bits, epi, a, sx, hs) == hipSuccess ? W4_OK : W4_ERR_LAUNCH;
+}
+
+extern "C" size_t w4_a8_workspace_bytes(int T, int K) {
+  if (T < 0 || K <= 0 || T > kMaxDim || K > kMaxDim || K % 64) return 0;
+  return a8_ws_bytes(T, K);
+}
+
+extern "C" int w4_quantize_a8(const uint16_t* x, int T, int K, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (T < 0 || K <= 0 || T > kMaxDim || K > kMaxDim || K % 64) return W4_ERR_INVALID_ARG;
+  if (T == 0) return W4_OK;
+  if (!x) return W4_ERR_INVALID_ARG;
+  if (!aligned16(x)) return W4_ERR_MISALIGNED;
+  int st = check_a8_ws(workspace, workspace_bytes, T, K, {span(x, (size_t)T * K * 2)});
+  if (st != W4_OK) return st;
+  st = device_check();
+  if (st != W4_OK) return st;
+  int8_t* xq = static_cast<int8_t*>(workspace);
+  float* sx = reinterpret_cast<float*>(static_cast<char*>(workspace) + align16((size_t)T * K));
+  return w4::launch_a8_quant(reinterpret_cast<const _Float16*>(x), T, K, xq, sx,
+                             static_cast<hipStream_t>(stream)) == hipSuccess ? W4_OK : W4_ERR_LAUNCH;
+}
+
+extern "C" int w4_linear_a8(const uint16_t* x, const void* w, const uint16_t* scales, const uint16_t* zeros,
+                            int T, int N, int K, int bits, int group, uint16_t* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return run_a8(W4_OP_LINEAR, x, w, scales, zeros, nullptr, T, N, K, bits, group, out, workspace,
+                workspace_bytes, stream);
+}
+
+extern "C" int w4_linear_swiglu_a8(const uint16_t* x, const void* w_pair, const uint16_t* scales_pair,
+                                   const uint16_t* zeros_pair, int T, int N, int K, int bits, int group,
+                                   uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_a8(W4_OP_SWIGLU, x, w_pair, scales_pair, zeros_pair, nullptr, T, N, K, bits, group, out,
+                workspace, workspace_bytes, stream);
+}
+
+extern "C" int w4_linear_add_a8(const uint16_t* x, const void* w, const uint16_t* scales,
+                                const uint16_t* zeros, const uint16_t* residual, int T, int N, int K,
+                                int bits, int group, uint16_t* out, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return run_a8(W4_OP_ADD, x, w, scales, zeros, residual, T, N, K, bits, group, out, workspace,
+                workspace_bytes, stream);
 }
 
 extern "C" size_t w4_bf16_workspace_bytes(int T, int K) {

@@ -119,6 +119,10 @@ inline hipError_t launch_stream16(int bits, int epi, const KArgs& a, hipStream_t
 }
 // narrow: token tiles of tn (32 or 64) columns; T > tn runs ceil(T / tn) token blocks side by side
 hipError_t launch_narrow(int tn, int bits, int epi, const KArgs& a, hipStream_t stream);
+// A8 route (a8.hip): int8 activations with a scale per 64 columns, and the int8 GEMM over them
+// (a.x holds the int8 codes; sx the scales, [ceil(K/128)][T][2])
+hipError_t launch_a8_quant(const _Float16* x, int T, int K, int8_t* xq, float* sx, hipStream_t stream);
+hipError_t launch_a8(int bits, int epi, const KArgs& a, const float* sx, hipStream_t stream);
 // bf16 activations [T][K] -> fp16 X[t] * 2^-e_t in xh and e_t in xexp (bf16.hip)
 hipError_t launch_bf16_prep(const uint16_t* x, int T, int K, _Float16* xh, int* xexp, hipStream_t stream);
 hipError_t launch_wide(int bits, int epi, const KArgs& a, hipStream_t stream);    // any T

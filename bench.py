@@ -56,6 +56,13 @@ WORKLOADS = {
     # 256 x 512: latency, not bandwidth (the weights fit in L2); reported in us, its GB/s figure
     # is not representative of the weight stream
     "tiny": ("tiny", (1,), "linear"),
+    # route-boundary sweep shapes (--route-sweep), not part of the default run
+    "q5_k5120": ("q5_k5120", (1, 64), "linear"),
+    "q5_down": ("q5_down", (1, 64), "linear"),
+    "q4_k17408": ("q4_k17408", (1, 64), "linear"),
+    "q5_k8192": ("q5_k8192", (1, 64), "linear"),
+    "q5_k12288": ("q5_k12288", (1, 64), "linear"),
+    "q4_k8192": ("q4_k8192", (1, 64), "linear"),
 }
 ALL_ORDER = ("decode", "tiny", "batched", "swiglu", "prefill")
 METRIC = "W4 GEMM effective weight GB/s (T<=64) and MFMA TFLOP/s (T>=1024), % roofline"
@@ -598,8 +605,22 @@ def route_sweep(args, w4, torch, widths, op, pws, xs, res, outs, copies, wstream
                   f"{wstream_alg / us / 1e3:7.0f} GB/s  {2.0 * T * rows * K / us / 1e6:7.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
     best = {T: min(r, key=r.get) for T, r in table.items()}
+    picks = {T: w4.route_name(w4.route_for(op, bits, int(T), N, K)) for T in table}
+    # the same table as markdown (stderr): one row per width, the fastest route and the public
+    # calls' choice, marked with its excess over the fastest when that is above 3 %
+    names = [w4.route_name(i) for i in range(w4.route_count())
+             if any(w4.route_name(i) in r for r in table.values())]
+    md = [f"## {args.workload}: N={N}, K={K}, {bits}-bit, {('linear', 'SwiGLU pair', 'LinearAdd')[op]}, us per launch", "",
+          "| T | " + " | ".join(names) + " | fastest | public call picks |",
+          "|---" * (len(names) + 3) + "|"]
+    for T, r in table.items():
+        extra = r[picks[T]] / r[best[T]] - 1.0
+        note = f" (+{100 * extra:.0f} %)" if extra > 0.03 else ""
+        md.append(f"| {T} | " + " | ".join(f"{r[n]:.2f}" if n in r else "" for n in names) +
+                  f" | {best[T]} | {picks[T]}{note} |")
+    print("\n".join(md), file=sys.stderr, flush=True)
     print(json.dumps({"route_sweep": args.workload, "N": N, "K": K, "bits": bits,
-                      "cold_copies": copies, "us": table, "fastest": best}))
+                      "cold_copies": copies, "us": table, "fastest": best, "picks": picks}))
     return 0
 
 

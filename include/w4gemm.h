@@ -231,8 +231,11 @@ typedef struct {
 
 /* out_p[T][N_p] = fp16_rne(X . dequant(W_p)^T) for p < nparents (1 .. W4_MAX_PARENTS), all
  * reading x [T][K].  For T <= 64 and K <= 5120 one kernel launch covers every matrix (each
- * workgroup runs the code width of its matrix); otherwise the call launches the route
- * w4_route_for picks for each matrix, one after another on `stream`.  Validation as w4_linear
+ * workgroup runs the code width of its matrix) with the streaming kernel of that width (the
+ * routes mfma_stream_t16 / _t32 / _t64 for T <= 16 / 32 / 64: each output equals that route's
+ * single-matrix result bit for bit, which for 5-bit matrices at T > 32 is not the route
+ * w4_linear picks); otherwise the call launches the route w4_route_for picks for each matrix,
+ * one after another on `stream`.  Validation as w4_linear
  * for every matrix, and no output may overlap another matrix's output, packed data or x
  * (W4_ERR_ALIAS).  parents: host array, read during the call only. */
 int w4_linear_grouped(const uint16_t* x, const w4_parent* parents, int nparents, int T, int K,

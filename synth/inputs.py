@@ -76,6 +76,27 @@ CONFIGS: Dict[str, dict] = {
     "prefill": dict(
         mats=[("w", 5120, 6144)], bits=5, zero=("const", 16), scale=(0.0025, 0.01),
         x_sigma=1.0, outliers=8, Ts=(1024, 4096), op="add"),
+    # shapes for route-boundary sweeps (not measured configurations): the 5-bit input projection
+    # rows at K = 5120, the 5-bit down projection [5120, 17408], and 5120-row matrices at
+    # K = 8192, 12288 (5-bit) and 8192, 17408 (4-bit) between the two
+    "q5_k5120": dict(
+        mats=[("w", 12288, 5120)], bits=5, zero=("const", 16), scale=(0.0025, 0.01),
+        x_sigma=1.0, outliers=8, Ts=(1, 64), op="linear"),
+    "q5_down": dict(
+        mats=[("w", 5120, 17408)], bits=5, zero=("const", 16), scale=(0.0025, 0.01),
+        x_sigma=1.0, outliers=8, Ts=(1, 64), op="linear"),
+    "q5_k8192": dict(
+        mats=[("w", 5120, 8192)], bits=5, zero=("const", 16), scale=(0.0025, 0.01),
+        x_sigma=1.0, outliers=8, Ts=(1, 64), op="linear"),
+    "q5_k12288": dict(
+        mats=[("w", 5120, 12288)], bits=5, zero=("const", 16), scale=(0.0025, 0.01),
+        x_sigma=1.0, outliers=8, Ts=(1, 64), op="linear"),
+    "q4_k8192": dict(
+        mats=[("w", 5120, 8192)], bits=4, zero=("uniform", 6, 9), scale=(0.005, 0.02),
+        x_sigma=1.0, outliers=8, Ts=(1, 64), op="linear"),
+    "q4_k17408": dict(
+        mats=[("w", 5120, 17408)], bits=4, zero=("uniform", 6, 9), scale=(0.005, 0.02),
+        x_sigma=1.0, outliers=8, Ts=(1, 64), op="linear"),
 }
 
 OUTLIER_FACTOR = 30.0

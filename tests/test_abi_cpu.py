@@ -47,11 +47,29 @@ def test_route_table_domains_cover_every_width():
     assert w4.route_name(n) is None and w4.route_name(-1) is None
     for op in (w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD):
         for bits in (4, 5):
-            for T in list(range(1, 130)) + [255, 256, 1000, 1024, 1025, 4096, 65536]:
-                r = w4.route_for(op, bits, T, 4096, 5120)
-                assert 0 <= r < n
-                lo, hi = w4.route_domain(r)
-                assert lo <= T <= hi, (op, bits, T, r)
+            for K in (512, 5120, 6144, 17408):
+                for T in list(range(1, 130)) + [255, 256, 1000, 1024, 1025, 4096, 65536]:
+                    r = w4.route_for(op, bits, T, 4096, K)
+                    assert 0 <= r < n
+                    lo, hi = w4.route_domain(r)
+                    assert lo <= T <= hi, (op, bits, T, K, r)
+
+
+@pytest.mark.parametrize("op,bits,T,K,route", [
+    # K <= 5120: streaming to 16 tokens, its 32-row ring to 32, then the 64-row ring for 4-bit
+    # single matrices and the narrow kernel for 5-bit codes and the SwiGLU pair
+    (0, 4, 16, 5120, "mfma_stream_t16"), (0, 5, 17, 5120, "mfma_stream_t32"),
+    (2, 4, 64, 5120, "mfma_stream_t64"), (0, 5, 33, 5120, "mfma_narrow_t64"),
+    (1, 4, 64, 5120, "mfma_narrow_t64"),
+    # K > 5120: streaming to 4 tokens, split K to 20, narrow beyond
+    (0, 5, 4, 6144, "mfma_stream_t16"), (0, 5, 5, 6144, "mfma_splitk_t32"),
+    (2, 4, 20, 17408, "mfma_splitk_t32"), (0, 4, 21, 8192, "mfma_narrow_t32"),
+    (0, 5, 64, 12288, "mfma_narrow_t64"),
+    # the SwiGLU pair at K > 5120 never takes split K
+    (1, 5, 16, 6144, "mfma_stream_t16"), (1, 5, 17, 6144, "mfma_narrow_t32"),
+])
+def test_route_choice_follows_measured_crossovers(op, bits, T, K, route):
+    assert w4.route_name(w4.route_for(op, bits, T, 5120, K)) == route
 
 
 def test_route_for_rejects_bad_shapes():

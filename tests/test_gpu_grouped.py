@@ -1,6 +1,8 @@
 """GPU tier: the grouped call (several packed matrices, 4- or 5-bit, over one activation, each
-with its own output).  Each output must equal, bit for bit, what the single-matrix call gives
-for that matrix (same kernels, same summation order), and match the fp64 oracle.  Small shapes
+with its own output).  Each output must equal, bit for bit, the single-matrix launch of the
+route the grouped call runs for that matrix (for T <= 64 and K <= 5120 the streaming route of
+its width: same kernel, same summation order; otherwise the route w4_linear picks), and match
+the fp64 oracle.  Small shapes
 span ragged row tiles, a half k-block (K % 128 == 64) and every slice and ring mode of the
 one-launch path (T <= 4, 5..8, 9..16, 17..32, 33..64) plus a width above it (one launch per
 matrix); the full-size cases
@@ -21,6 +23,15 @@ from gpu_util import assert_close, canon, to_np
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
+
+
+def _single(xd, pw, T, K):
+    """The single-matrix launch of the kernel the grouped call runs for this matrix."""
+    if T <= 64 and K <= 5120:
+        name = "mfma_stream_t16" if T <= 16 else "mfma_stream_t32" if T <= 32 else "mfma_stream_t64"
+        rid = {w4.route_name(i): i for i in range(w4.route_count())}[name]
+        return w4.linear_route(rid, w4.OP_LINEAR, xd, pw)
+    return w4.linear(xd, pw)
 
 
 def _weights(rng, specs, K):
@@ -45,7 +56,7 @@ def test_grouped_matches_single_and_oracle(specs, K, T):
     xd = torch.from_numpy(x).to(DEV)
     print(f"case grouped specs={specs} K={K} T={T}", flush=True)
     ys = w4.linear_grouped(xd, pws)
-    singles = [w4.linear(xd, pw) for pw in pws]
+    singles = [_single(xd, pw, T, K) for pw in pws]
     torch.cuda.synchronize()
     for i, (y, y1, w, (_, b)) in enumerate(zip(ys, singles, ws, specs)):
         assert np.array_equal(to_np(y).view(np.uint16), to_np(y1).view(np.uint16)), (i, specs, K, T)
@@ -63,7 +74,7 @@ def test_grouped_repeat_and_stream_order():
         x, _ = make_activations(rng, T, K, 1.0, 0)
         xd = torch.from_numpy(x).to(DEV)
         ys = w4.linear_grouped(xd, pws[::-1] if T % 2 else pws)
-        ref = [w4.linear(xd, pw) for pw in (pws[::-1] if T % 2 else pws)]
+        ref = [_single(xd, pw, T, K) for pw in (pws[::-1] if T % 2 else pws)]
         torch.cuda.synchronize()
         for y, r in zip(ys, ref):
             assert np.array_equal(to_np(y).view(np.uint16), to_np(r).view(np.uint16)), T
@@ -85,7 +96,7 @@ def test_grouped_full_size(specs, T):
     xd = torch.from_numpy(x).to(DEV)
     print(f"case grouped full specs={specs} T={T}", flush=True)
     ys = w4.linear_grouped(xd, pws)
-    singles = [w4.linear(xd, pw) for pw in pws]
+    singles = [_single(xd, pw, T, K) for pw in pws]
     torch.cuda.synchronize()
     for i, (y, y1, w, (N, b)) in enumerate(zip(ys, singles, ws, specs)):
         assert np.array_equal(to_np(y).view(np.uint16), to_np(y1).view(np.uint16)), (i, specs, T)

@@ -157,30 +157,31 @@ def test_fractional_zero_points(route):
 
 def test_public_calls_match_their_route():
     """w4_linear / _swiglu / _add run exactly the route w4_route_for names (bitwise)."""
-    N, K = 256, 512
-    for op in (w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD):
-        for bits in (4, 5):
-            for T in (1, 2, 4, 8, 16, 24, 32, 48, 64, 65, 200):
-                ws, x, r = _case(N, K, T, bits, op, seed=T + op)
-                pw = _pack(ws, op, bits)
-                xd = torch.from_numpy(x).to(DEV)
-                rd = torch.from_numpy(r).to(DEV) if r is not None else None
-                if op == w4.OP_SWIGLU:
-                    y = w4.linear_swiglu(xd, pw)
-                elif op == w4.OP_ADD:
-                    y = w4.linear_add(xd, pw, rd)
-                else:
-                    y = w4.linear(xd, pw)
-                rid = w4.route_for(op, bits, T, N, K)
-                y2 = w4.linear_route(rid, op, xd, pw, residual=rd)
-                assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (op, bits, T)
+    N = 256
+    for op, bits, K in [(o, b, k) for o in (w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD)
+                        for b in (4, 5) for k in (512, 6144)]:
+        for T in (1, 2, 4, 5, 8, 16, 20, 24, 32, 48, 64, 65, 200):
+            ws, x, r = _case(N, K, T, bits, op, seed=T + op + K)
+            pw = _pack(ws, op, bits)
+            xd = torch.from_numpy(x).to(DEV)
+            rd = torch.from_numpy(r).to(DEV) if r is not None else None
+            if op == w4.OP_SWIGLU:
+                y = w4.linear_swiglu(xd, pw)
+            elif op == w4.OP_ADD:
+                y = w4.linear_add(xd, pw, rd)
+            else:
+                y = w4.linear(xd, pw)
+            rid = w4.route_for(op, bits, T, N, K)
+            y2 = w4.linear_route(rid, op, xd, pw, residual=rd)
+            assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (op, bits, T, K)
 
 
 @pytest.mark.parametrize("K", [6144, 12352, 17408])
 @pytest.mark.parametrize("route", sorted(ROUTE_TS))
 def test_long_k(route, K):
-    """K ranges that take the 8-, 16-block and looping variants of the streaming kernels,
-    including a half-empty last k-block (12352 = 96.5 blocks)."""
+    """K ranges that take the 8-, 16-block and looping variants of the streaming kernels and
+    the split-K kernel's tail alone (6 blocks per wave) or its loop and tail (13 and 17), with a
+    half-empty last k-block (12352 = 96.5 blocks)."""
     N = 48
     for op in (w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD):
         for bits in (4, 5):

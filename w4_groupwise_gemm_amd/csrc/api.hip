@@ -128,25 +128,37 @@ int device_check() {
 // the decode, batched-decode, SwiGLU-pair and 5120-row prefill shapes); the reasons are given
 // case by case below.
 int pick_route(int op, int bits, int T, int N, int K) {
-  (void)bits;
-  // The streaming route holds the activation slice of each wave in LDS up to K = 5120 (16 token
-  // rows), which keeps it ahead up to its 16-token limit there (11264 x 5120, T = 16: 11.4 us
-  // against 15.8 with split K); beyond, its activation fragments ride in the load ring and split
-  // K takes over after T = 10.  The SwiGLU pair streams two row tiles per workgroup, which
-  // keeps the streaming route ahead up to 16 tokens at any K.  For 17-32 tokens and K <= 5120
-  // the streaming kernel's 32-row activation ring is ahead of the narrow kernel (11264 x 5120,
-  // T = 32: 12.5 vs 16.1 us; SwiGLU pair T = 24: 40.6 vs 46.0); beyond that K the narrow kernel
-  // is ahead of split K from T = 17 (15.8 vs 16.1 us at T = 18).
-  if (T <= 10 || (T <= 16 && (op == W4_OP_SWIGLU || K <= 5120))) return R_N16;
-  if (T <= 32 && K <= 5120) return R_S32;
-  if (T <= 16) return R_SPLITK;
-  if (T <= 32) return R_N32;
-  // 33-64 tokens: the streaming kernel's one-slot 64-row ring is a little ahead of the narrow
-  // kernel for single matrices (11264 x 5120, T = 64: 17.9 vs 19.9 us), not for the SwiGLU
-  // pair, whose two-tile workgroups take 4 rounds of the one workgroup per compute unit that
-  // the ring allows (61.5 vs 57.5 us)
-  if (T <= 64 && K <= 5120 && op != W4_OP_SWIGLU) return R_S64;
-  if (T <= 64) return R_N64;
+  // Crossovers measured per route on cold weights (5120 output rows unless named; us):
+  //  * K <= 5120: the streaming route holds each wave's activation slice in LDS, which keeps it
+  //    ahead up to its 16-token limit (4-bit, T = 16: 10.7 against 14.7 with split K; 5-bit
+  //    13.1 against 23.3); for 17-32 tokens its 32-row ring leads (T = 32: 13.2 against 15.8
+  //    for the narrow kernel, 5-bit 15.1 against 18.0; SwiGLU pair 44.4 against 45.7).
+  //  * K > 5120: beyond 4 tokens the streaming route's activation fragments ride in its load
+  //    ring and split K leads to T = 20 (6144 / 8192 / 12288 / 17408 columns at T = 16, 5-bit:
+  //    15.0 / 16.8 / 23.4 / 31.5 against 18.4 / 21.2 / 30.7 / 43.7 streamed and 15.5 / 18.6 /
+  //    25.7 / 35.1 narrow); from T = 24 the narrow kernel leads (15.6 / 18.7 / 25.7 / 34.9
+  //    against 16.5 / 19.4 / 27.4 / 37.3).  The SwiGLU pair streams two row tiles per
+  //    workgroup, which keeps the streaming route ahead up to 16 tokens, and the narrow kernel
+  //    after that (split K: 41.7 against 32.1 streamed at T = 16, 44.0 against 42.9 narrow at 20).
+  //  * 33-64 tokens: the streaming kernel's one-slot 64-row ring is ahead for single 4-bit
+  //    matrices at K <= 5120 (T = 64: 17.7 against 20.5); the narrow kernel is ahead for 5-bit
+  //    codes (22.3 against 26.8), at longer K (8192 x 5-bit: 23.1 against 23.3) and for the
+  //    SwiGLU pair, whose two-tile workgroups take 4 rounds of the one workgroup per compute
+  //    unit that the ring allows (59.1 against 61.5).
+  if (K <= 5120) {
+    if (T <= 16) return R_N16;
+    if (T <= 32) return R_S32;
+    if (T <= 64) return (op == W4_OP_SWIGLU || bits == 5) ? R_N64 : R_S64;
+  } else if (op == W4_OP_SWIGLU) {
+    if (T <= 16) return R_N16;
+    if (T <= 32) return R_N32;
+    if (T <= 64) return R_N64;
+  } else {
+    if (T <= 4) return R_N16;
+    if (T <= 20) return R_SPLITK;
+    if (T <= 32) return R_N32;
+    if (T <= 64) return R_N64;
+  }
   // Above 64 tokens the wide kernel's workgroups (about 128 rows x 128 tokens each) leave most
   // compute units idle until there are about 128 of them; below that the narrow kernel run as
   // side-by-side 64-token blocks is faster (5120 rows: 34 vs 73 us at T = 128, 67 vs 73 at 384,

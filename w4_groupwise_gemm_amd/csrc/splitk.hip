@@ -87,7 +87,7 @@ __device__ __forceinline__ void block_math(const Blk<NP>& b, uint32_t magic, boo
   }
 }
 
-template <int BITS, int NP, int NW, int KPW, int D, int EPI, bool LOOP>
+template <int BITS, int NP, int NW, int D, int EPI>
 __global__ __launch_bounds__(NW * 64) void splitk_kernel(KArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
@@ -112,33 +112,44 @@ __global__ __launch_bounds__(NW * 64) void splitk_kernel(KArgs a) {
 #pragma unroll
   for (int p = 0; p < NP; ++p) acc[p] = f32x16{};
 
-  // Without LOOP the launcher guarantees one chunk per wave (kb1 - kb0 <= KPW); with it, very
-  // long K runs in chunks of KPW blocks (the ring drains between chunks).
-  for (int c0 = kb0; LOOP ? c0 < kb1 : c0 == kb0; c0 += KPW) {
-    const int nb = min(KPW, kb1 - c0);
-    Blk<NP> ring[KPW];
-    // the first D blocks unconditionally (a wave with fewer blocks re-reads its last one): the
-    // compiler then counts the loads in flight exactly and waits for one block at a time
-    static_assert(D <= KPW, "ring deeper than the chunk");
+  // Rolling ring of D + 1 block slots: block i sits in slot i mod (D + 1).  Before block i is
+  // multiplied, block i + D goes into the slot that block i - 1 freed, so D blocks stay in
+  // flight behind the one in use.  Slot indices are compile-time constants (rounds of D + 1
+  // blocks are unrolled), which keeps the ring in registers at any K.
+  Blk<NP> ring[D + 1];
+  auto consume = [&](const Blk<NP>& b, int kb) {
+    // exact wave-uniform test: are all zero-points of this block integers (1024 + z exact)?
+    bool exact = true;
+    const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f};
 #pragma unroll
-    for (int i = 0; i < D; ++i) issue<BITS, NP>(ring[i], R, a, m, pair0, ntiles, c0 + min(i, nb - 1), xoff);
+    for (int p = 0; p < NP; ++p)
+      exact = exact && (__builtin_bit_cast(uint32_t, (as_h2(b.zp[p]) + c1024) - c1024) == b.zp[p]);
+    const bool half = half_last && kb == KB - 1;
+    if (__ballot(exact) == ~0ull)
+      block_math<BITS, NP, true>(b, magic, half, acc);
+    else
+      block_math<BITS, NP, false>(b, magic, half, acc);
+  };
+  // the first D blocks unconditionally (a wave with fewer blocks re-reads its last one, a wave
+  // with none reads block 0 and never uses it)
+  const int klast = max(kb1 - 1, 0);
 #pragma unroll
-    for (int i = 0; i < KPW; ++i) {
-      if (i + D < KPW && i + D < nb) issue<BITS, NP>(ring[i + D], R, a, m, pair0, ntiles, c0 + i + D, xoff);
-      if (i < nb) {
-        // exact wave-uniform test: are all zero-points of this block integers (1024 + z exact)?
-        bool exact = true;
-        const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f};
+  for (int i = 0; i < D; ++i) issue<BITS, NP>(ring[i], R, a, m, pair0, ntiles, min(kb0 + i, klast), xoff);
+  // whole rounds whose loads are all in range: unconditional, so the compiler's wait counts
+  // stay exact across the loop
+  int c = kb0;
+  for (; c + 2 * D < kb1; c += D + 1) {
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
-          exact = exact && (__builtin_bit_cast(uint32_t, (as_h2(ring[i].zp[p]) + c1024) - c1024) == ring[i].zp[p]);
-        const bool half = half_last && c0 + i == KB - 1;
-        if (__ballot(exact) == ~0ull)
-          block_math<BITS, NP, true>(ring[i], magic, half, acc);
-        else
-          block_math<BITS, NP, false>(ring[i], magic, half, acc);
-      }
+    for (int j = 0; j <= D; ++j) {
+      issue<BITS, NP>(ring[(j + D) % (D + 1)], R, a, m, pair0, ntiles, c + j + D, xoff);
+      consume(ring[j], c + j);
     }
+  }
+  // the last (at most 2 D) blocks
+#pragma unroll
+  for (int j = 0; j < 2 * D; ++j) {
+    if (c + j + D < kb1) issue<BITS, NP>(ring[(j + D) % (D + 1)], R, a, m, pair0, ntiles, c + j + D, xoff);
+    if (c + j < kb1) consume(ring[j % (D + 1)], c + j);
   }
 
   // fixed-order sum of the NW partials: red[w][p][v][lane]
@@ -181,24 +192,14 @@ __global__ __launch_bounds__(NW * 64) void splitk_kernel(KArgs a) {
 
 constexpr int kNW = 8;  // waves per workgroup (K split)
 
-template <int BITS, int NP, int KPW, int EPI, bool LOOP>
+template <int BITS, int NP, int EPI>
 hipError_t run_k(const KArgs& a, hipStream_t stream) {
   const int ntiles = a.rows / 16;
   const int npairs = (ntiles + 1) / 2;
   const int grid = (npairs + NP - 1) / NP;
   const size_t lds = (size_t)kNW * NP * 16 * 64 * 4;
-  constexpr int D = (NP == 1 && !LOOP) ? 3 : 2;  // blocks in flight per wave (register budget)
-  return launch_kernel(&splitk_kernel<BITS, NP, kNW, KPW, D, EPI, LOOP>, dim3(grid), dim3(kNW * 64), lds,
-                       stream, a);
-}
-
-template <int BITS, int NP, int EPI>
-hipError_t pick_kpw(const KArgs& a, hipStream_t stream) {
-  const int nbw = (a.KB + kNW - 1) / kNW;
-  if (nbw <= 5) return run_k<BITS, NP, 5, EPI, false>(a, stream);
-  if (nbw <= 8) return run_k<BITS, NP, 8, EPI, false>(a, stream);
-  if (nbw <= 16) return run_k<BITS, NP, 16, EPI, false>(a, stream);
-  return run_k<BITS, NP, 5, EPI, true>(a, stream);
+  constexpr int D = NP == 1 ? 3 : 1;  // blocks in flight per wave (register budget)
+  return launch_kernel(&splitk_kernel<BITS, NP, kNW, D, EPI>, dim3(grid), dim3(kNW * 64), lds, stream, a);
 }
 
 template <int BITS, int EPI>
@@ -207,9 +208,9 @@ hipError_t pick_np(const KArgs& a, hipStream_t stream) {
   // still leaves a workgroup for most compute units; one pair otherwise
   const int npairs = (a.rows / 16 + 1) / 2;
   if constexpr (BITS == 4) {
-    if (npairs >= 2 * 160) return pick_kpw<BITS, 2, EPI>(a, stream);
+    if (npairs >= 2 * 160) return run_k<BITS, 2, EPI>(a, stream);
   }
-  return pick_kpw<BITS, 1, EPI>(a, stream);
+  return run_k<BITS, 1, EPI>(a, stream);
 }
 
 template <int BITS>

@@ -621,8 +621,12 @@ hipError_t run_k(const KArgs& a, hipStream_t stream) {
                        lds, stream, a, xdim);
 }
 
-// k-blocks per wave: one unrolled chunk for K <= 16384 (exactly the wave's block count up to
-// 5, so that no ring slot is a re-read), a chunk loop beyond.
+// k-blocks per wave: one unrolled chunk (exactly the wave's block count up to 5, so that no
+// ring slot is a re-read), up to 8 blocks with a 4-row activation slice and up to 16 with
+// fragments in the ring; a chunk loop beyond.  A 4-row slice of more than 8 blocks per wave
+// would take more than 80 KB of LDS (96 KB at K = 12288), one workgroup per compute unit, and
+// a 5120-row launch (320 workgroups) would then run in two rounds: 19.8 us at T = 1 with 5-bit
+// codes, against 11.1 at K = 8192 and 23.0 at K = 17408 (8-block chunks).
 template <int BITS, int MODE, int RT, int XL, int EPI>
 hipError_t run(const KArgs& a, hipStream_t stream) {
   const int nbw = (a.KB + kNW - 1) / kNW;
@@ -635,7 +639,9 @@ hipError_t run(const KArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;  // 8- and 16-row slices are picked for K <= 5120 only
   } else {
     if (nbw <= 8) return run_k<BITS, MODE, RT, XL, EPI, 8, false>(a, stream);
-    if (nbw <= 16) return run_k<BITS, MODE, RT, XL, EPI, 16, false>(a, stream);
+    if constexpr (XL == 0) {
+      if (nbw <= 16) return run_k<BITS, MODE, RT, XL, EPI, 16, false>(a, stream);
+    }
     return run_k<BITS, MODE, RT, XL, EPI, 8, true>(a, stream);
   }
 }

@@ -112,8 +112,11 @@ def main() -> int:
     ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of rotated weight copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--route", type=int, default=-1, help="force one route (bench of a schedule)")
-    ap.add_argument("--probe", choices=["copy", "read"], default=None,
-                    help="run only the plain copy/read kernel of libw4probe.so (counter reference)")
+    ap.add_argument("--probe", choices=["copy", "read", "bcast", "lds"], default=None,
+                    help="run only a kernel of libw4probe.so: plain copy / read (counter reference, "
+                         "HBM read rate), bcast (every workgroup reads the same --probe-mb buffer "
+                         "from L2; sweeps grids, registers and direct-to-LDS), lds (LDS read rate "
+                         "per compute unit; sweeps waves per workgroup and grids)")
     ap.add_argument("--probe-mb", type=float, default=256.0)
     ap.add_argument("--probe-cold", action="store_true",
                     help="read probe over rotated copies (--cold-bytes GiB), graph-replayed "
@@ -637,11 +640,56 @@ def run_probe(args) -> int:
     P.w4probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
     P.w4probe_read_u.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                  ctypes.c_void_p]
+    P.w4probe_bcast.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_void_p]
+    P.w4probe_lds.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     nbytes = int(args.probe_mb * 1e6) // 4096 * 4096
     dev = torch.device("cuda:0")
     grid = args.probe_grid
     stream = torch.cuda.current_stream()
     sh = ctypes.c_void_p(stream.cuda_stream)
+    if args.probe in ("bcast", "lds"):
+        sink = torch.empty(16, dtype=torch.uint8, device=dev)
+        buf = torch.randint(0, 255, (max(nbytes, 16),), dtype=torch.uint8, device=dev)
+
+        def timed(launch, n):
+            for _ in range(3):
+                if launch() != 0:
+                    raise RuntimeError("probe launch failed")
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / n
+
+        table = {}
+        if args.probe == "bcast":
+            for dma in (0, 1):
+                for g_wg in (256, 512, 768, 1024):
+                    us = timed(lambda: P.w4probe_bcast(buf.data_ptr(), nbytes, sink.data_ptr(), g_wg, dma, sh), 200)
+                    moved = g_wg * nbytes
+                    table[f"{'lds' if dma else 'vgpr'}_g{g_wg}"] = {
+                        "us": us, "TBs": moved / us / 1e6, "B_per_clk_per_CU": moved / 256 / (us * 1e-6 * 2.4e9)}
+                    print(f"[probe] bcast {nbytes / 1e3:.0f} KB x {g_wg} workgroups, "
+                          f"{'direct-to-LDS' if dma else 'registers'}: {us:.2f} us "
+                          f"{moved / us / 1e6:.1f} TB/s", file=sys.stderr, flush=True)
+        else:
+            iters = 2000
+            for threads in (256, 512, 1024):
+                for g_wg in (256, 512, 1024):
+                    us = timed(lambda: P.w4probe_lds(iters, sink.data_ptr(), g_wg, threads, sh), 10)
+                    moved = g_wg * threads * iters * 8 * 16
+                    table[f"t{threads}_g{g_wg}"] = {
+                        "us": us, "B_per_clk_per_CU": moved / 256 / (us * 1e-6 * 2.4e9)}
+                    print(f"[probe] lds {threads // 64} waves x {g_wg} workgroups: {us:.1f} us "
+                          f"{moved / 256 / (us * 1e-6 * 2.4e9):.1f} B/clk per compute unit",
+                          file=sys.stderr, flush=True)
+        print(json.dumps({"probe": args.probe, "bytes": nbytes if args.probe == "bcast" else None,
+                          "clock_GHz_assumed": 2.4, "compute_units": 256, "table": table}))
+        return 0
     if args.probe_cold:
         if args.probe != "read":
             raise SystemExit("--probe-cold applies to --probe read")

@@ -359,7 +359,8 @@ def run_workload(args, wname, torch, w4, cpu_timing):
         value = len(widths) * wstream_alg / (ms_per_step * 1e6)
         unit_v = "GB/s"
 
-    context = context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, dev)
+    context = context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, dev, wname,
+                              pws, copies)
 
     cpu, parity = None, None
     if not args.no_cpu_baseline:
@@ -393,7 +394,8 @@ def run_workload(args, wname, torch, w4, cpu_timing):
 
 
 
-def context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, dev):
+def context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, dev, wname, pws,
+                    copies):
     """Figures reported beside the measured path, never as its value.
 
     * Parents that share one activation (the batched workload): each parent as a call of its
@@ -403,6 +405,12 @@ def context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, de
     * Prefill widths: a dense fp16 GEMM of the same shape through the vendor library (random
       fp16 weights held as [K][N] for x @ W and as [N][K] for linear(x, W)), over rotated cold
       weight copies: the ceiling a dequantising kernel is compared with.
+    * Decode and prefill: the same calls with bf16 activations (w4_linear_bf16 /
+      w4_linear_add_bf16: the per-token exponent pass plus the fp16 kernel), on the same cold
+      copies, beside the fp16 call.
+    * Decode: one verify-width decode step of three calls (the input projection of this
+      workload, a SwiGLU pair [17408, 5120] and a LinearAdd down projection [5120, 17408]),
+      launched eagerly from Python and replayed from a per-width graph set (VerifyGraphs).
     Both timed over >= --cold-bytes of rotated copies, HIP events on the launch stream, median
     of 5 (our calls replayed from a graph, the library's launched eagerly)."""
     if args.route >= 0 or args.no_graph or pair:
@@ -478,7 +486,102 @@ def context_figures(args, w4, torch, wl, widths, bits, K, N, op, pair, per_T, de
                                                   "fp16 weights of the same shape, cold copies", "per_T": dense}
         if op in (w4.OP_ADD, w4.OP_LINEAR) and bits in (4, 5):
             out["a8_route"] = a8_route(w4, torch, args, timed, wl, widths, bits, K, N, op, dev)
+    if wname in ("decode", "prefill") and len(wl.weights) == 1:
+        out["bf16_activations"] = bf16_context(w4, torch, timed, wl, widths, N, K, op, pws, copies,
+                                               per_T, dev)
+    if wname == "decode":
+        out["verify_step_graphs"] = verify_step_context(w4, torch, pws[0], K, dev)
     return out or None
+
+
+def bf16_context(w4, torch, timed, wl, widths, N, K, op, pws, copies, per_T, dev):
+    """bf16 activations and outputs (and residual) through the public bf16 calls, over the
+    workload's cold weight copies, graph-replayed: per width the whole call (exponent pass +
+    kernel) beside the fp16 call of per_T."""
+    res = {}
+    for T in widths:
+        x = torch.from_numpy(np.ascontiguousarray(wl.x[:T])).to(dev).to(torch.bfloat16)
+        r = (torch.from_numpy(np.ascontiguousarray(wl.r[:T])).to(dev).to(torch.bfloat16)
+             if op == w4.OP_ADD else None)
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(16, w4.bf16_workspace_bytes(T, K)), dtype=torch.uint8, device=dev)
+        if op == w4.OP_ADD:
+            us = timed(lambda c: w4.linear_add_bf16(x, pws[c], r, out=y, workspace=ws), copies)
+        else:
+            us = timed(lambda c: w4.linear_bf16(x, pws[c], out=y, workspace=ws), copies)
+        res[str(T)] = {"us": us, "fp16_us": per_T[str(T)]["us_mean"],
+                       "extra_us": us - per_T[str(T)]["us_mean"]}
+    return {"what": "bf16 activations, outputs (and residual): per-token exponent pass + fp16 "
+                    "kernel, cold copies, graph-replayed", "per_T": res}
+
+
+def verify_step_context(w4, torch, pw_in, K, dev, widths=(1, 2, 4, 8), steps=20, layers=8):
+    """A decode step at a verify width: `layers` layers of three calls each -- y = linear(x,
+    W_in), h = swiglu(x, W_gu), o = linear_add(h, W_down, x_res) -- launched eagerly from Python
+    and replayed from the width's recorded graph (one launch per step), mean over `steps` steps
+    between synchronisations.  Two scales: the decode shapes (W_in this workload's matrix, W_gu a
+    [17408, 5120] pair, W_down [5120, 17408]; each kernel 8-25 us, so Python stays ahead of the
+    GPU) and small ones (W_in [2048, 1024], W_gu [2048, 1024], W_down [1024, 2048]; each kernel a
+    few us, so the launches dominate).  4-bit random packed codes, integer zero-points and N(0, 1)
+    activations (the kernels' cost does not depend on the values); the layers share one set of
+    weights, hot in the Infinity Cache: this isolates the launch overhead the graph removes."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1)
+
+    def rand_pw(N, Kc, pair):
+        rows = 2 * N if pair else N
+        nb = w4.packed_bytes(rows, Kc, 4)
+        nsz = w4.packed_sz_bytes(rows, Kc) // 2
+        w = torch.randint(0, 256, (nb,), dtype=torch.uint8, device=dev, generator=gen)
+        s = torch.full((nsz,), 0.01, dtype=torch.float16, device=dev).view(torch.int16)
+        z = torch.full((nsz,), 8.0, dtype=torch.float16, device=dev).view(torch.int16)
+        return w4.PackedWeight(w, s, z, N, Kc, 4, pair)
+
+    scales = {
+        "decode_shapes": (pw_in, rand_pw(17408, K, True), rand_pw(5120, 17408, False)),
+        "small_shapes": (rand_pw(2048, 1024, False), rand_pw(2048, 1024, True), rand_pw(1024, 2048, False)),
+    }
+    out = {"what": f"decode step of {layers} layers x 3 calls (input projection, SwiGLU pair, LinearAdd "
+                   "down projection), eager Python launches vs. one graph-set replay per step, hot weights",
+           "layers": layers}
+    for name, (p_in, p_gu, p_dn) in scales.items():
+        vg = w4.VerifyGraphs()
+        st = vg.stream
+        res = {}
+        for T in widths:
+            x = torch.randn((T, p_in.K), generator=gen, device=dev).to(torch.float16)
+            xr = torch.randn((T, p_dn.N), generator=gen, device=dev).to(torch.float16)
+            y = torch.empty((T, p_in.N), dtype=torch.float16, device=dev)
+            h = torch.empty((T, p_gu.N), dtype=torch.float16, device=dev)
+            o = torch.empty((T, p_dn.N), dtype=torch.float16, device=dev)
+
+            def step(T_, x=x, xr=xr, y=y, h=h, o=o, p_in=p_in, p_gu=p_gu, p_dn=p_dn):
+                for _ in range(layers):
+                    w4.linear(x, p_in, out=y, stream=st)
+                    w4.linear_swiglu(x, p_gu, out=h, stream=st)
+                    w4.linear_add(h, p_dn, xr, out=o, stream=st)
+
+            def per_step_us(fn):
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+                for _ in range(steps):
+                    fn()
+                e1.record(st)
+                torch.cuda.synchronize()
+                return e0.elapsed_time(e1) * 1e3 / steps
+
+            with torch.cuda.stream(st):
+                eager = per_step_us(lambda: step(T))
+            vg.run(T, step)
+            torch.cuda.synchronize()
+            graph = per_step_us(lambda: vg.run(T))
+            res[str(T)] = {"eager_us": eager, "graph_us": graph, "graph_over_eager": graph / eager}
+        vg.close()
+        out[name] = res
+    return out
 
 
 def a8_route(w4, torch, args, timed, wl, widths, bits, K, N, op, dev):

@@ -37,6 +37,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup barrier without a memory fence.  The fence that __syncthreads() adds would wait for
+// every outstanding load of the wave, including the ones meant to stay in flight; the waits are
+// explicit instead (producers: vmcnt for their own loads; consumers: lgkmcnt for their LDS
+// reads).  The "memory" clobber keeps the compiler from moving memory operations across it.
+__device__ __forceinline__ void arrive_wait() {
+  // lgkmcnt(0) as a builtin, so that the compiler's own wait insertion knows every earlier LDS
+  // read has completed; the barrier itself as volatile asm with a memory clobber
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // (a & mask) | c in one v_and_or_b32 (the compiler can otherwise form and + and + or3)
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t c) {
   uint32_t r;

@@ -53,17 +53,6 @@ struct CodeStage {
   static constexpr int kOps = NP * 2 * (BITS == 5 ? 2 : 1) + 2;
 };
 
-// Workgroup barrier without a memory fence.  The fence that __syncthreads() adds would wait for
-// every outstanding load of the wave, including the ones meant to stay in flight; the waits are
-// explicit instead (producers: vmcnt for their own loads; consumers: lgkmcnt for their LDS
-// reads).  The "memory" clobber keeps the compiler from moving memory operations across it.
-__device__ __forceinline__ void arrive_wait() {
-  // lgkmcnt(0) as a builtin, so that the compiler's own wait insertion knows every earlier LDS
-  // read has completed; the barrier itself as volatile asm with a memory clobber
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt 63 (no wait), expcnt 7, lgkmcnt 0
-  asm volatile("s_barrier" ::: "memory");
-}
-
 // Direct-to-LDS loads: lane L's bytes land at lds + SIZE * L.
 __device__ __forceinline__ void lds_load16(const __amdgpu_buffer_rsrc_t& r, char* lds, int voffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,

@@ -110,8 +110,13 @@ constexpr bool slice_dma() {
 // HB: K is not a multiple of 128, so the last k-block holds one group only (without it the
 // per-block test for that case, and its branches, compile away).
 // bx: the workgroup's index among those of this matrix (its row tiles are bx RT ..).
+// ring0 / ring1 (two-slot 32-row ring only): slot 0 and slot 1 of every wave, one array each.
+// A direct-to-LDS refill is a write the compiler cannot place within an array, so before any
+// LDS read it waits for the newest refill into the same array; with the two slots in distinct
+// arrays, reading slot (i + 1) % 2 no longer waits for the refill of slot i % 2 (and for every
+// load issued before it).
 template <int BITS, int MODE, int RT, int NW, int KPW, int D, int XL, int EPI, bool LOOP, bool HB>
-__device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
+__device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx, char* ring0, char* ring1) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int BLK = block_bytes(BITS);
   const int lane = threadIdx.x & 63;
@@ -144,11 +149,19 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
   constexpr int TH = RING ? XL / 16 : 1;  // 16-token groups per weight fragment
   constexpr int NSLOT = XL == 32 ? 2 : 1;
   constexpr int XBLK = XL * 256;
-  char* const xs = smem + (size_t)wave * (RING ? NSLOT * XBLK : XDMA ? xdim * XBLK : XL * xdim * 2);
+  char* const xs = NSLOT == 2 ? nullptr
+                  : smem + (size_t)wave * (RING ? NSLOT * XBLK : XDMA ? xdim * XBLK : XL * xdim * 2);
+  // slot of local block i (i is a constant once the block loop is unrolled)
+  auto xslot = [&](int i) -> char* {
+    if constexpr (NSLOT == 2)
+      return (i % 2 ? ring1 : ring0) + (size_t)wave * XBLK;
+    else
+      return xs;
+  };
   // 16-byte chunk c (0..15) of token row t of local block i
   auto xchunk = [&](int i, int t, int c) -> const char* {
     if constexpr (RING)
-      return xs + (i % NSLOT) * XBLK + t * 256 + ((c ^ (t & 15)) << 4);
+      return xslot(i) + t * 256 + ((c ^ (t & 15)) << 4);
     else if constexpr (XDMA)
       return xs + i * XBLK + t * 256 + ((c ^ t) << 4);
     else
@@ -221,7 +234,7 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
       for (int h = 0; h < XL / 4; ++h) {
         const int t = 4 * h + (lane >> 4);
         const int off = (t * a.K + kb * 128 + (((lane & 15) ^ (t & 15)) << 3)) * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (__attribute__((address_space(3))) void*)(xs + (i % NSLOT) * XBLK + h * 1024),
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (__attribute__((address_space(3))) void*)(xslot(i) + h * 1024),
                                                  16, off, 0, 0, 0);
       }
     };
@@ -423,8 +436,10 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
   // ---- fixed-order combination of the NW partial sums, then the epilogue
   __syncthreads();
   if constexpr (MODE == MODE_MFMA) {
-    // red[w][h][rt][lane]: wave w's partial sums of token half h, row tile rt
-    f32x4* red = reinterpret_cast<f32x4*>(smem);
+    // red[w][h][rt][lane]: wave w's partial sums of token half h, row tile rt (the two-slot
+    // ring's first array holds them there: NW x 2 x RT KB within its NW x 8 KB)
+    f32x4* red = reinterpret_cast<f32x4*>(NSLOT == 2 ? ring0 : smem);
+    static_assert(NSLOT != 2 || TH * RT * 1024 <= XBLK, "reduction fits the ring's first array");
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       red[((wave * TH + 0) * RT + rt) * 64 + lane] = acc[rt];
@@ -492,7 +507,12 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx) {
 
 template <int BITS, int MODE, int RT, int NW, int KPW, int D, int XL, int EPI, bool LOOP, bool HB>
 __global__ __launch_bounds__(NW * 64) void stream_kernel(KArgs a, int xdim) {
-  stream_body<BITS, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(a, xdim, blockIdx.x);
+  if constexpr (XL == 32) {
+    __shared__ __attribute__((aligned(16))) char ring0[NW * 32 * 256], ring1[NW * 32 * 256];
+    stream_body<BITS, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(a, xdim, blockIdx.x, ring0, ring1);
+  } else {
+    stream_body<BITS, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(a, xdim, blockIdx.x, nullptr, nullptr);
+  }
 }
 
 // Grouped launch: several matrices (4- or 5-bit) that share one activation, each with its own
@@ -509,10 +529,18 @@ __global__ __launch_bounds__(NW * 64) void stream_grouped_kernel(GArgs g, int xd
   int p = 0;
   while (p + 1 < g.n && (int)blockIdx.x >= g.end[p]) ++p;
   const int bx = blockIdx.x - (p > 0 ? g.end[p - 1] : 0);
-  if (g.bits[p] == 5)
-    stream_body<5, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(g.a[p], xdim, bx);
-  else
-    stream_body<4, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(g.a[p], xdim, bx);
+  if constexpr (XL == 32) {
+    __shared__ __attribute__((aligned(16))) char ring0[NW * 32 * 256], ring1[NW * 32 * 256];
+    if (g.bits[p] == 5)
+      stream_body<5, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(g.a[p], xdim, bx, ring0, ring1);
+    else
+      stream_body<4, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(g.a[p], xdim, bx, ring0, ring1);
+  } else {
+    if (g.bits[p] == 5)
+      stream_body<5, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(g.a[p], xdim, bx, nullptr, nullptr);
+    else
+      stream_body<4, MODE, RT, NW, KPW, D, XL, EPI, LOOP, HB>(g.a[p], xdim, bx, nullptr, nullptr);
+  }
 }
 
 constexpr int kNW = 8;  // waves per workgroup (K split)
@@ -596,6 +624,7 @@ constexpr int ring_depth() {
 // passed to the kernel), or the final reduction of the NW partial sums if that is larger.
 template <int MODE, int RT, int XL, bool DMA>
 size_t stream_lds(int nbc, int xdim) {
+  if constexpr (XL == 32) return 0;  // the two-slot ring and its reduction live in static arrays
   const size_t x = XL == 32 ? (size_t)kNW * 2 * 32 * 256
                  : XL == 64 ? (size_t)kNW * 64 * 256
                  : DMA ? (size_t)kNW * nbc * XL * 256 : XL == 4 ? (size_t)kNW * 4 * xdim * 2 : 0;

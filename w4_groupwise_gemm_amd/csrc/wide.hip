@@ -39,18 +39,6 @@ using namespace w4dev;
 using namespace t32;
 using w4layout::block_bytes;
 
-// A-operand words of one 32-row pair and one k-block, for this lane.  Set S (0 / 1) is the
-// 16-byte load of k-steps (j, S), j = 0..3; the lane's row is pair row lane % 32, its k half
-// h = lane / 32.  In packed terms: 16-lane group (lane / 16) reads tile a, b, a, b of the pair,
-// and the source lane inside that tile is lane % 16 + 16 (S + 2 h), whose k slots are
-// 64 (j / 2) + 16 (S + 2 h) + 8 (j % 2) + e.
-template <int BITS>
-struct PairCodes {
-  u32x4 cw[2];
-  uint32_t hw[2];   // high-bit planes (5-bit only)
-  uint32_t sp, zp;  // this lane's row: fp16 scale / zero-point pairs (groups 0, 1 of the block)
-};
-
 // The share of the fifth pair that one wave computes: its two dwords (k-steps) of one set.
 template <int BITS>
 struct ShareCodes {
@@ -58,27 +46,6 @@ struct ShareCodes {
   uint32_t hw;
   uint32_t sp, zp;
 };
-
-// Every offset below is lane-dependent, so it goes in the lane operand; the tile index is
-// clamped to the last tile (an odd tile count leaves the second tile of the last pair empty:
-// its rows are computed from the clamped tile and never stored).
-template <int BITS>
-__device__ __forceinline__ void load_pair(PairCodes<BITS>& c, const Rsrcs& R, const KArgs& a,
-                                          const LaneMap& m, int pair, int ntiles, int kb) {
-  constexpr int BLK = block_bytes(BITS);
-  const int tile = min(2 * pair + m.th, ntiles - 1);
-  const int bi = tile * a.KB + kb;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    c.cw[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.w, bi * BLK + m.slot16[s], 0, 0));
-    if constexpr (BITS == 5)
-      c.hw[s] = __builtin_amdgcn_raw_buffer_load_b32(R.w, bi * BLK + 1024 + m.slot16[s] / 4, 0, 0);
-    else
-      c.hw[s] = 0;
-  }
-  c.sp = __builtin_amdgcn_raw_buffer_load_b32(R.s, bi * 4 * a.szw + m.szoff, 0, 0);
-  c.zp = __builtin_amdgcn_raw_buffer_load_b32(R.z, bi * 4 * a.szw + m.szoff, 0, 0);
-}
 
 // Wave W's share of pair `pair`: set S = W / 2, dwords j = 2 (W % 2) and 2 (W % 2) + 1.
 template <int BITS, int W>

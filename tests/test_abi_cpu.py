@@ -57,10 +57,13 @@ def test_route_table_domains_cover_every_width():
 
 @pytest.mark.parametrize("op,bits,T,K,route", [
     # K <= 5120: streaming to 16 tokens, its 32-row ring to 32, then the 64-row ring for 4-bit
-    # single matrices and the narrow kernel for 5-bit codes and the SwiGLU pair
+    # single matrices and the narrow kernel for 5-bit codes; the SwiGLU pair streams to 8
+    # tokens and takes the evenly spread narrow kernel beyond
     (0, 4, 16, 5120, "mfma_stream_t16"), (0, 5, 17, 5120, "mfma_stream_t32"),
     (2, 4, 64, 5120, "mfma_stream_t64"), (0, 5, 33, 5120, "mfma_narrow_t64"),
-    (1, 4, 64, 5120, "mfma_narrow_t64"),
+    (1, 4, 8, 5120, "mfma_stream_t16"), (1, 4, 9, 5120, "mfma_bal_t32"),
+    (1, 4, 32, 5120, "mfma_bal_t32"), (1, 4, 33, 5120, "mfma_bal_t64"),
+    (1, 4, 64, 5120, "mfma_bal_t64"),
     # K > 5120: streaming to 4 tokens, split K to 20, narrow beyond
     (0, 5, 4, 6144, "mfma_stream_t16"), (0, 5, 5, 6144, "mfma_splitk_t32"),
     (2, 4, 20, 17408, "mfma_splitk_t32"), (0, 4, 21, 8192, "mfma_narrow_t32"),

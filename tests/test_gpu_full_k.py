@@ -20,7 +20,7 @@ DEV = "cuda:0"
 N = 784
 # route -> widths: 4-row slice, 8-row slice, 16-row slice, 32-row ring, 64-row ring
 CASES = [("mfma_stream_t16", t) for t in (4, 5, 8, 9, 16)] + [("mfma_stream_t32", t) for t in (17, 32)] + \
-        [("mfma_stream_t64", t) for t in (33, 64)]
+        [("mfma_stream_t64", t) for t in (33, 64)] + [("mfma_bal_t32", 24), ("mfma_bal_t64", 64)]
 
 
 @pytest.mark.parametrize("K", [5120, 5056])

@@ -29,6 +29,8 @@ ROUTE_TS = {
     "mfma_narrow_tiled": (1, 33, 65, 129, 200),
     "mfma_stream_t32": (1, 5, 16, 17, 24, 32),
     "mfma_stream_t64": (1, 17, 33, 40, 64),
+    "mfma_bal_t32": (1, 3, 17, 32),
+    "mfma_bal_t64": (1, 33, 40, 64),
 }
 
 

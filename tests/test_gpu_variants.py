@@ -32,6 +32,8 @@ ROUTE_TS = {
     "mfma_narrow_tiled": (65, 130),
     "mfma_stream_t32": (17, 32),
     "mfma_stream_t64": (33, 64),
+    "mfma_bal_t32": (5, 32),
+    "mfma_bal_t64": (33, 64),
 }
 
 

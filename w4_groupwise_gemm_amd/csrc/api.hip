@@ -28,7 +28,8 @@ enum RouteKind {
   KIND_WIDE = 3,
   KIND_SPLITK = 4,
   KIND_STREAM32 = 5,
-  KIND_STREAM64 = 6
+  KIND_STREAM64 = 6,
+  KIND_BALANCED = 7
 };
 
 struct Route {
@@ -48,11 +49,13 @@ const Route kRoutes[] = {
     {"mfma_narrow_tiled", 1, INT_MAX, KIND_NARROW, 64},
     {"mfma_stream_t32", 1, 32, KIND_STREAM32, 32},
     {"mfma_stream_t64", 1, 64, KIND_STREAM64, 64},
+    {"mfma_bal_t32", 1, 32, KIND_BALANCED, 32},
+    {"mfma_bal_t64", 1, 64, KIND_BALANCED, 64},
 };
 constexpr int kNumRoutes = sizeof(kRoutes) / sizeof(kRoutes[0]);
 // route ids (indices into kRoutes; R_N16 is the 16-token streaming route)
 enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5, R_NTILED = 6, R_S32 = 7,
-       R_S64 = 8 };
+       R_S64 = 8, R_B32 = 9, R_B64 = 10 };
 
 constexpr int kMaxDim = 1 << 24;
 
@@ -142,13 +145,23 @@ int pick_route(int op, int bits, int T, int N, int K) {
   //    after that (split K: 41.7 against 32.1 streamed at T = 16, 44.0 against 42.9 narrow at 20).
   //  * 33-64 tokens: the streaming kernel's one-slot 64-row ring is ahead for single 4-bit
   //    matrices at K <= 5120 (T = 64: 17.7 against 20.5); the narrow kernel is ahead for 5-bit
-  //    codes (22.3 against 26.8), at longer K (8192 x 5-bit: 23.1 against 23.3) and for the
-  //    SwiGLU pair, whose two-tile workgroups take 4 rounds of the one workgroup per compute
-  //    unit that the ring allows (59.1 against 61.5).
+  //    codes (22.7 against 26.8) and at longer K (8192 x 5-bit: 23.3 against 23.6).
+  //  * The SwiGLU pair at K <= 5120 (17408 x 2 rows): the narrow kernel with its rows spread
+  //    evenly over one workgroup per compute unit (4-5 pairs each) leads from 12 tokens (T = 12
+  //    / 16 / 24 / 32 / 64: 31.1 / 31.5 / 31.4 / 31.7 / 51.7 us against 31.8 / 32.1 streamed,
+  //    40.5 / 42.3 with the 32-row ring, 58.7 narrow in pairs of two); the streaming route's
+  //    8-row slice keeps T <= 8 (24.8 against 31.2).  For single matrices of 5120 rows the
+  //    even spread (1-2 tiles per workgroup) trails the narrow kernel's pairs by 2-8 %.
   if (K <= 5120) {
-    if (T <= 16) return R_N16;
-    if (T <= 32) return R_S32;
-    if (T <= 64) return (op == W4_OP_SWIGLU || bits == 5) ? R_N64 : R_S64;
+    if (op == W4_OP_SWIGLU) {
+      if (T <= 8) return R_N16;
+      if (T <= 32) return R_B32;
+      if (T <= 64) return R_B64;
+    } else {
+      if (T <= 16) return R_N16;
+      if (T <= 32) return R_S32;
+      if (T <= 64) return bits == 5 ? R_N64 : R_S64;
+    }
   } else if (op == W4_OP_SWIGLU) {
     if (T <= 16) return R_N16;
     if (T <= 32) return R_N32;
@@ -197,16 +210,17 @@ int launch_route(int route, int op, const void* x, const void* w, const void* s,
   switch (R.kind) {
     case KIND_GEMV: e = w4::launch_gemv(bits, epi, a, st); break;
     case KIND_STREAM: e = w4::launch_stream16(bits, epi, a, st); break;
-    case KIND_NARROW: e = w4::launch_narrow(R.tn, bits, epi, a, st); break;
+    case KIND_NARROW: e = w4::launch_narrow(R.tn, false, bits, epi, a, st); break;
+    case KIND_BALANCED: e = w4::launch_narrow(R.tn, true, bits, epi, a, st); break;
     case KIND_WIDE: e = w4::launch_wide(bits, epi, a, st); break;
     case KIND_SPLITK: e = w4::launch_splitk(bits, epi, a, st); break;
     case KIND_STREAM32:
       // the 32-row activation ring of the streaming kernel covers K <= 5120 (five k-blocks per
       // wave); longer rows run this route's schedule on the narrow kernel's 32-token tile
-      e = K <= 5120 ? w4::launch_stream32(bits, epi, a, st) : w4::launch_narrow(32, bits, epi, a, st);
+      e = K <= 5120 ? w4::launch_stream32(bits, epi, a, st) : w4::launch_narrow(32, false, bits, epi, a, st);
       break;
     case KIND_STREAM64:  // likewise with 64-row tiles
-      e = K <= 5120 ? w4::launch_stream64(bits, epi, a, st) : w4::launch_narrow(64, bits, epi, a, st);
+      e = K <= 5120 ? w4::launch_stream64(bits, epi, a, st) : w4::launch_narrow(64, false, bits, epi, a, st);
       break;
     default: return W4_ERR_DOMAIN;
   }

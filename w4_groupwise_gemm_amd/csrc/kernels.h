@@ -117,8 +117,16 @@ inline hipError_t launch_stream16(int bits, int epi, const KArgs& a, hipStream_t
     default: return hipErrorInvalidValue;
   }
 }
-// narrow: token tiles of tn (32 or 64) columns; T > tn runs ceil(T / tn) token blocks side by side
-hipError_t launch_narrow(int tn, int bits, int epi, const KArgs& a, hipStream_t stream);
+// narrow: token tiles of tn (32 or 64) columns; T > tn runs ceil(T / tn) token blocks side by
+// side.  balanced: rows spread evenly over one workgroup per compute unit (up to 5 tile pairs
+// each); otherwise one or two pairs per workgroup.
+hipError_t launch_narrow_b4(int tn, bool balanced, int epi, const KArgs& a, hipStream_t stream);
+hipError_t launch_narrow_b5(int tn, bool balanced, int epi, const KArgs& a, hipStream_t stream);
+inline hipError_t launch_narrow(int tn, bool balanced, int bits, int epi, const KArgs& a,
+                                hipStream_t stream) {
+  return bits == 5 ? launch_narrow_b5(tn, balanced, epi, a, stream)
+                   : launch_narrow_b4(tn, balanced, epi, a, stream);
+}
 // A8 route (a8.hip): int8 activations with a scale per 64 columns, and the int8 GEMM over them
 // (a.x holds the int8 codes; sx the scales, [ceil(K/128)][T][2])
 hipError_t launch_a8_quant(const _Float16* x, int T, int K, int8_t* xq, float* sx, hipStream_t stream);

@@ -63,28 +63,33 @@ __device__ __forceinline__ void lds_load4(const __amdgpu_buffer_rsrc_t& r, char*
                                            voffset, 0, 0, 0);
 }
 
-// Codes, high planes, scales and zero-points of block kb for the workgroup's pairs.  Tile
-// indices are clamped to the last tile (an odd tile count leaves an empty second tile in the
-// last pair; its rows are never stored).
+// A byte offset past the end of every buffer (all tensors are below 2 GiB): a load from it
+// returns zeros without touching memory, and still counts as one load in the wave's counter.
+constexpr int kNoLoad = 0x7FFFFFF0;
+
+// Codes, high planes, scales and zero-points of block kb for the workgroup's tiles t0 ..
+// t0 + nt - 1 (1 <= nt <= 2 NP).  Stage slots past the workgroup's own tiles (an empty second
+// tile in the last pair, or pairs the instance has room for but this workgroup lacks) are
+// filled from kNoLoad: the load count per block stays a compile-time constant, no byte is
+// fetched for them, and their rows are never stored.
 template <int BITS, int NP>
-__device__ __forceinline__ void load_codes(const Rsrcs& R, const KArgs& a, char* st, int pair0,
-                                           int ntiles, int kb, int lane) {
+__device__ __forceinline__ void load_codes(const Rsrcs& R, const KArgs& a, char* st, int t0,
+                                           int nt, int kb, int lane) {
   using CS = CodeStage<BITS, NP>;
   constexpr int BLK = block_bytes(BITS);
 #pragma unroll
   for (int i = 0; i < 2 * NP; ++i) {
-    const int tile = min(2 * pair0 + i, ntiles - 1);
-    const int bi = tile * a.KB + kb;
-    lds_load16(R.w, st + CS::kLo + i * 1024, bi * BLK + lane * 16);
-    if constexpr (BITS == 5) lds_load4(R.w, st + CS::kHi + i * 256, bi * BLK + 1024 + lane * 4);
+    const int bi = (t0 + i) * a.KB + kb;
+    lds_load16(R.w, st + CS::kLo + i * 1024, i < nt ? bi * BLK + lane * 16 : kNoLoad);
+    if constexpr (BITS == 5)
+      lds_load4(R.w, st + CS::kHi + i * 256, i < nt ? bi * BLK + 1024 + lane * 4 : kNoLoad);
   }
   // scales / zero-points: the 2 NP tiles' blocks of szb bytes each, 16 bytes per lane, by the
-  // lanes that cover them (at least 8 of the 64: one instruction each, whatever the group
-  // size); tiles past the last one re-read it, and those words are never read
+  // lanes that cover them (at least 8 of the 64: one instruction each, whatever the group size)
   const int szb = 4 * a.szw;
   if (lane * 16 < 2 * NP * szb) {
-    const int tile = min(2 * pair0 + lane * 16 / szb, ntiles - 1);
-    const int off = (tile * a.KB + kb) * szb + lane * 16 % szb;
+    const int i = lane * 16 / szb;
+    const int off = i < nt ? ((t0 + i) * a.KB + kb) * szb + lane * 16 % szb : kNoLoad;
     lds_load16(R.s, st + CS::kS, off);
     lds_load16(R.z, st + CS::kZ, off);
   }
@@ -233,10 +238,18 @@ __device__ __forceinline__ void consumer(const KArgs& a, const char* cring, cons
     consume<BITS, NP, NTT, NC, DC, DX, C, false>(a, cring, xring, acc);
 }
 
+// Rows of each workgroup: units of `ut` tiles (1, or 2 for the SwiGLU pair, whose gate and up
+// tiles stay together), `units` of them in all.  chunk > 0: workgroup b takes units
+// b chunk .. b chunk + chunk - 1; chunk == 0: the units are spread evenly over the grid (sizes
+// differ by at most one unit), so a grid of one workgroup per compute unit runs in one round.
+struct Part {
+  int units, ut, chunk;
+};
+
 // Workgroup = NC consumer waves (math) + 1 code producer + 1 activation producer.  LDS: the code
 // ring (DC stages), then the activation ring (DX stages); the reduction at the end reuses it.
 template <int BITS, int NP, int NTT, int NC, int DC, int DX, int EPI>
-__global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
+__global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a, Part part) {
   using CS = CodeStage<BITS, NP>;
   constexpr int BN = 32 * NTT, XB = BN * 256;
   // token block blockIdx.y: tokens BN y .. BN y + BN - 1 (more than one only when T > BN)
@@ -251,10 +264,22 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const cring = smem;
   char* const xring = smem + DC * CS::kBytes;
+  // the zero-point votes sit past both rings (the reduction at the end may reuse them)
+  int* const votes = reinterpret_cast<int*>(xring + DX * XB);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ntiles = a.rows / 16;
-  const int pair0 = blockIdx.x * NP;
+  // this workgroup's tiles t0 .. t0 + nt - 1 (1 <= nt <= 2 NP; the host sizes the grid so)
+  int u0, u1;
+  if (part.chunk > 0) {
+    u0 = blockIdx.x * part.chunk;
+    u1 = min(u0 + part.chunk, part.units);
+  } else {
+    u0 = (int)((long long)blockIdx.x * part.units / gridDim.x);
+    u1 = (int)((long long)(blockIdx.x + 1) * part.units / gridDim.x);
+  }
+  const int t0 = u0 * part.ut;
+  const int nt = min(u1 * part.ut, ntiles) - t0;
   const int KB = a.KB;
 
   Rsrcs R;
@@ -273,17 +298,16 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
   // of this workgroup's zero-points integers (1024 + z exact in fp16)?  The votes meet in LDS
   // at barrier B(-1), which the producers reach as soon as their first block has landed (a
   // fenced barrier here would hold them until their whole prologue had).
-  __shared__ int votes[NC];
   if (wave == NC) {
 #pragma unroll
     for (int j = 0; j < DC; ++j)
-      load_codes<BITS, NP>(R, a, cring + j * CS::kBytes, pair0, ntiles, min(j, KB - 1), lane);
+      load_codes<BITS, NP>(R, a, cring + j * CS::kBytes, t0, nt, min(j, KB - 1), lane);
   } else if (wave == NC + 1) {
 #pragma unroll
     for (int j = 0; j < DX; ++j) load_x<BN>(R, a, xring + j * XB, voff, min(j, KB - 1));
   } else {
-    const int zbase = 2 * pair0 * KB * 4 * a.szw;  // bytes: zero-points of the workgroup's tiles
-    const int zbytes = 2 * NP * KB * 4 * a.szw;
+    const int zbase = t0 * KB * 4 * a.szw;  // bytes: zero-points of the workgroup's tiles
+    const int zbytes = nt * KB * 4 * a.szw;
     const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f};
     constexpr int STEP = 64 * NC * 16;  // bytes per load instruction of all consumers
     bool exact = true;
@@ -320,7 +344,7 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
 
   if (wave == NC) {
     produce<DC, CS::kOps>(KB, [&](int st, int kb) {
-      load_codes<BITS, NP>(R, a, cring + st * CS::kBytes, pair0, ntiles, kb, lane);
+      load_codes<BITS, NP>(R, a, cring + st * CS::kBytes, t0, nt, kb, lane);
     });
   } else if (wave == NC + 1) {
     produce<DX, BN / 4>(KB, [&](int st, int kb) { load_x<BN>(R, a, xring + st * XB, voff, kb); });
@@ -375,73 +399,106 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a) {
     for (int idx = wave; idx < NP * NTT * 2; idx += NC) {
       const int it = idx >> 1, q = idx & 1;
       const int p = it / NTT, tt = it % NTT;
-      const int pair = pair0 + p, t = 32 * tt + (lane & 31);
-      if (t >= a.T || 2 * pair >= ntiles) continue;
+      const int t = 32 * tt + (lane & 31);
+      if (t >= a.T || 2 * p >= nt) continue;
       const f32x4 g = {sum(p, tt, 4 * q), sum(p, tt, 4 * q + 1), sum(p, tt, 4 * q + 2), sum(p, tt, 4 * q + 3)};
       const f32x4 u = {sum(p, tt, 8 + 4 * q), sum(p, tt, 9 + 4 * q), sum(p, tt, 10 + 4 * q), sum(p, tt, 11 + 4 * q)};
-      store_quad<EPI>(a, t, 16 * pair + 8 * q + 4 * h, g, u);
+      store_quad<EPI>(a, t, 8 * (t0 + 2 * p) + 8 * q + 4 * h, g, u);
     }
   } else {
     // (item, register quad q) pairs: pair rows 8q + 4h + 0..3
     for (int idx = wave; idx < NP * NTT * 4; idx += NC) {
       const int it = idx >> 2, q = idx & 3;
       const int p = it / NTT, tt = it % NTT;
-      const int pair = pair0 + p, t = 32 * tt + (lane & 31);
-      if (t >= a.T || 2 * pair >= ntiles) continue;
-      if (q >= 2 && 2 * pair + 1 >= ntiles) continue;  // odd tile count: no second tile
+      const int t = 32 * tt + (lane & 31);
+      if (t >= a.T || 2 * p + (q >> 1) >= nt) continue;  // no such tile in this workgroup
       const f32x4 v = {sum(p, tt, 4 * q), sum(p, tt, 4 * q + 1), sum(p, tt, 4 * q + 2), sum(p, tt, 4 * q + 3)};
-      store_quad<EPI>(a, t, 32 * pair + 8 * q + 4 * h, v, f32x4{});
+      store_quad<EPI>(a, t, 16 * (t0 + 2 * p) + 8 * q + 4 * h, v, f32x4{});
     }
   }
 }
 
 template <int BITS, int NP, int NTT, int EPI>
-hipError_t run(const KArgs& a, hipStream_t stream) {
+hipError_t run(const KArgs& a, int grid, Part part, hipStream_t stream) {
   using CS = CodeStage<BITS, NP>;
   constexpr int BN = 32 * NTT;
   constexpr int NC = 4;  // consumer waves
-  constexpr int DX = 4;  // activation stages
+  // activation stages: as deep as the activation producer's load counter allows (its loads
+  // share the memory queues with the weight stream, so they see its latency)
+  constexpr int DX = 63 / (BN / 4) + 1;
   constexpr int DCMAX = 63 / CS::kOps + 1;
   constexpr int DC = DCMAX < 12 ? DCMAX : 12;  // code stages
-  const int ntiles = a.rows / 16;
-  const int npairs = (ntiles + 1) / 2;
-  const int grid = (npairs + NP - 1) / NP;
-  const size_t rings = (size_t)DC * CS::kBytes + (size_t)DX * BN * 256;
-  const size_t red = (size_t)NC * NP * NTT * 16 * 64 * 4;
-  const size_t lds = rings > red ? rings : red;
+  constexpr size_t rings = (size_t)DC * CS::kBytes + (size_t)DX * BN * 256 + NC * sizeof(int);
+  constexpr size_t red = (size_t)NC * NP * NTT * 16 * 64 * 4;
+  constexpr size_t lds = rings > red ? rings : red;
+  static_assert(lds <= 160 * 1024, "LDS of one workgroup");
   const int ntb = (a.T + BN - 1) / BN;
   if (ntb > 65535) return hipErrorInvalidConfiguration;  // grid y limit (T above 4 million)
   return launch_kernel(&narrow_kernel<BITS, NP, NTT, NC, DC, DX, EPI>, dim3(grid, ntb),
-                       dim3(64 * (NC + 2)), lds, stream, a);
+                       dim3(64 * (NC + 2)), lds, stream, a, part);
 }
 
+constexpr int kCUs = 256;    // compute units of the chip (gfx950, MI350 series)
+constexpr int kMaxPairs = 5;  // largest instance (pairs per workgroup)
+
 template <int BITS, int NTT, int EPI>
-hipError_t pick_np(const KArgs& a, hipStream_t stream) {
+hipError_t pick_np(bool balanced, const KArgs& a, hipStream_t stream) {
   const int ntiles = a.rows / 16;
-  const int npairs = (ntiles + 1) / 2;
-  // Two pairs per workgroup (each activation block shared by 64 rows) while that still leaves a
-  // workgroup for most compute units; one pair otherwise.
-  if (npairs >= 2 * 160) return run<BITS, 2, NTT, EPI>(a, stream);
-  return run<BITS, 1, NTT, EPI>(a, stream);
+  if (!balanced) {
+    // Two pairs per workgroup (each activation block shared by 64 rows) while that still
+    // leaves a workgroup for most compute units; one pair otherwise.
+    const int npairs = (ntiles + 1) / 2;
+    const int np = npairs >= 2 * 160 ? 2 : 1;
+    const int grid = (npairs + np - 1) / np;
+    const Part part{npairs, 2, np};
+    return np == 2 ? run<BITS, 2, NTT, EPI>(a, grid, part, stream)
+                   : run<BITS, 1, NTT, EPI>(a, grid, part, stream);
+  }
+  // Balanced: one workgroup per compute unit (fewer when there are fewer units), each with an
+  // even share of the units; more workgroups only when a share would exceed kMaxPairs pairs.
+  const int ut = EPI == EPI_SWIGLU ? 2 : 1;
+  const int units = ntiles / ut;
+  const int cap = 2 * kMaxPairs / ut;  // units per workgroup
+  int grid = units < kCUs ? units : kCUs;
+  if ((units + grid - 1) / grid > cap) grid = (units + cap - 1) / cap;
+  const int per = (units + grid - 1) / grid;  // largest share
+  const int np = (per * ut + 1) / 2;
+  const Part part{units, ut, 0};
+  switch (np) {
+    case 1: return run<BITS, 1, NTT, EPI>(a, grid, part, stream);
+    case 2: return run<BITS, 2, NTT, EPI>(a, grid, part, stream);
+    case 3: return run<BITS, 3, NTT, EPI>(a, grid, part, stream);
+    case 4: return run<BITS, 4, NTT, EPI>(a, grid, part, stream);
+    default: return run<BITS, 5, NTT, EPI>(a, grid, part, stream);
+  }
 }
 
 template <int BITS, int EPI>
-hipError_t pick_nt(int tn, const KArgs& a, hipStream_t stream) {
-  if (tn <= 32) return pick_np<BITS, 1, EPI>(a, stream);
-  return pick_np<BITS, 2, EPI>(a, stream);
+hipError_t pick_nt(int tn, bool balanced, const KArgs& a, hipStream_t stream) {
+  if (tn <= 32) return pick_np<BITS, 1, EPI>(balanced, a, stream);
+  return pick_np<BITS, 2, EPI>(balanced, a, stream);
 }
 
 template <int BITS>
-hipError_t pick_epi(int tn, int epi, const KArgs& a, hipStream_t stream) {
-  if (epi == EPI_SWIGLU) return pick_nt<BITS, EPI_SWIGLU>(tn, a, stream);
-  if (epi == EPI_ADD) return pick_nt<BITS, EPI_ADD>(tn, a, stream);
-  return pick_nt<BITS, EPI_STORE>(tn, a, stream);
+hipError_t pick_epi(int tn, bool balanced, int epi, const KArgs& a, hipStream_t stream) {
+  if (epi == EPI_SWIGLU) return pick_nt<BITS, EPI_SWIGLU>(tn, balanced, a, stream);
+  if (epi == EPI_ADD) return pick_nt<BITS, EPI_ADD>(tn, balanced, a, stream);
+  return pick_nt<BITS, EPI_STORE>(tn, balanced, a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_narrow(int tn, int bits, int epi, const KArgs& a, hipStream_t stream) {
-  return bits == 5 ? pick_epi<5>(tn, epi, a, stream) : pick_epi<4>(tn, epi, a, stream);
+// One object per code width (W4_NARROW_BITS), so that the two compile in parallel.
+#if W4_NARROW_BITS == 4
+hipError_t launch_narrow_b4(int tn, bool balanced, int epi, const KArgs& a, hipStream_t stream) {
+  return pick_epi<4>(tn, balanced, epi, a, stream);
 }
+#elif W4_NARROW_BITS == 5
+hipError_t launch_narrow_b5(int tn, bool balanced, int epi, const KArgs& a, hipStream_t stream) {
+  return pick_epi<5>(tn, balanced, epi, a, stream);
+}
+#else
+#error "compile narrow.hip with -DW4_NARROW_BITS=4 or 5"
+#endif
 
 }  // namespace w4

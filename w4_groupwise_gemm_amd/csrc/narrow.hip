@@ -7,26 +7,34 @@
 //
 // gfx950 design.  At 17-64 tokens the weight stream still dominates the bytes, the activation
 // block (BN tokens x 128 columns, 8-16 KB) is needed by every workgroup, and the matrix-core
-// work per weight byte is 4-8x that of decode, so the kernel has to keep a deep stream of code
-// loads in flight while the math runs.  One wave's vector-memory counter is in order, so a wave
-// that waits for a recent load also waits for every older one; the roles are therefore split
-// between waves (warp specialisation), each with only one stream in its counter:
-//  * wave 4 streams the packed codes, scales and zero-points of the workgroup's NP 32-row tile
-//    pairs, LC blocks ahead, into an LDS ring (buffer_load ... lds: no registers, no copies);
-//  * wave 5 streams the activation tile of each block, LX blocks ahead, into a second LDS ring
-//    (16-byte chunks XOR-swizzled by token row, conflict-free reads);
-//  * waves 0-3 do the math.  The eight 16-k matrix-core steps of every 128-column block are
-//    split between them: wave w takes set S = w / 2, dwords 2 (w % 2) and 2 (w % 2) + 1 of each
-//    pair's packed block (the packed layout is the operand order of v_mfma_f32_32x32x16_f16 for
-//    a 32-row pair), dequantises its 8 bytes per lane per pair in registers and runs NTT
-//    matrix-core steps per fragment (B = 32 tokens).
-//  * One barrier per block: producers arrive once their loads for the block have landed,
-//    consumers once they have finished reading the previous block (its stages are then free).
-//    Loads past the last block re-read the last block into free stages, so the per-block load
-//    count, and with it every wait, is a compile-time constant.
-//  * The four consumers' partial sums are added in a fixed order through LDS (bitwise
-//    reproducible), then the epilogue (store / SwiGLU / residual add) writes fp16 quads.
-//  * Integer zero-points (checked exactly once per workgroup) select the short dequantisation.
+// work per weight byte is 4-8x that of decode, so the kernel has to keep a deep stream of loads
+// in flight while the math runs.  Every load is a direct-to-LDS buffer load (no registers, no
+// copies) into a ring of stages: a block's packed codes, high planes, scales and zero-points
+// (the packed layout, copied as is) and its activation tile (16-byte chunks XOR-swizzled by
+// token row: conflict-free reads).  One wave's vector-memory counter is in order, so a wave that
+// waits for a recent load also waits for every older one; two layouts keep each counter to one
+// in-order stream:
+//  * producer waves (warp specialisation): wave 4 streams the codes, scales and zero-points of
+//    the workgroup's NP 32-row tile pairs DC blocks ahead into a code ring, wave 5 the
+//    activation tiles DX blocks ahead into an activation ring; waves 0-3 do the math.  The two
+//    rings' depths are independent, which keeps many code bytes in flight when a block's
+//    activation tile is large against its codes (one or two pairs, 64 tokens).
+//  * self-loading waves (SELF): four waves, one per SIMD (so each may hold up to 512 registers:
+//    five pairs of 64-token accumulators fit without spilling), each issuing its share of every
+//    block's loads into a common ring of D stages and doing its share of the math.
+// In both, the eight 16-k matrix-core steps of every 128-column block are split between the four
+// math waves: wave w takes set S = w / 2, dwords 2 (w % 2) and 2 (w % 2) + 1 of each pair's
+// packed block (the packed layout is the operand order of v_mfma_f32_32x32x16_f16 for a 32-row
+// pair), dequantises its 8 bytes per lane per pair in registers and runs NTT matrix-core steps
+// per fragment (B = 32 tokens), reading each block's operands from LDS one block ahead.  One
+// fence-free barrier per block: a wave arrives once the loads it waits for have landed and it
+// has finished reading the previous block (whose stages are then refilled).  Loads past the last
+// block re-read the last block, so the per-block load count, and with it every wait, is a
+// compile-time constant.  Rows per workgroup: one or two pairs, or (balanced routes) an even
+// share of the row tiles for one workgroup per compute unit, up to five pairs.  The four partial
+// sums are added in a fixed order through LDS (bitwise reproducible), then the epilogue (store /
+// SwiGLU / residual add) writes fp16 quads.  Integer zero-points (checked exactly once per
+// workgroup) select the short dequantisation.
 #include "device.h"
 #include "kernels.h"
 #include "tile32.h"
@@ -130,8 +138,59 @@ __device__ __forceinline__ void produce(int KB, Issue issue) {
   }
 }
 
-// Steps of consumer C among NC: with 4 consumers, 2 consecutive 16-k steps (dwords J0, J0+1 of
-// set S of every pair's packed block); with 8, one.
+// Loads of one k-block, split over the NC waves of the workgroup: load j (0 .. kL - 1) is issued
+// by wave j % NC into the block's stage (code part cs, activation part xs).  In order: the 2 NP
+// low-plane tiles, (5-bit) their 2 NP high planes, the scale words, the zero-point words, then
+// the activation tile's BN / 4 loads of 4 token rows each.
+template <int BITS, int NP, int BN>
+struct BlockLoads {
+  static constexpr int kTiles = 2 * NP * (BITS == 5 ? 2 : 1);
+  static constexpr int kL = kTiles + 2 + BN / 4;
+  static constexpr int per_wave(int w, int nc) { return (kL - w + nc - 1) / nc; }
+};
+
+// Wave W's share of block kb's loads.  Stage slots past the workgroup's own tiles read nothing
+// (kNoLoad).  Activation tile: lane L of an instruction takes token row r0 + L/16 and stores LDS
+// chunk L%16, which holds source chunk (L%16) ^ (row & 15); the whole offset is in the
+// range-checked lane operand, so token rows beyond T lie past the end of the buffer and read as
+// zero, and columns beyond K inside the buffer (half-empty last block) read the next row,
+// whose k slots the math never uses.
+template <int BITS, int NP, int BN, int NC, int W>
+__device__ __forceinline__ void issue_block(const Rsrcs& R, const KArgs& a, char* cs, char* xs,
+                                            const int (&voff)[4], int t0, int nt, int kb, int lane) {
+  using CS = CodeStage<BITS, NP>;
+  using BL = BlockLoads<BITS, NP, BN>;
+  constexpr int BLK = block_bytes(BITS);
+#pragma unroll
+  for (int j = W; j < BL::kL; j += NC) {
+    if (j < 2 * NP) {
+      const int bi = (t0 + j) * a.KB + kb;
+      lds_load16(R.w, cs + CS::kLo + j * 1024, j < nt ? bi * BLK + lane * 16 : kNoLoad);
+    } else if (j < BL::kTiles) {
+      const int i = j - 2 * NP;
+      const int bi = (t0 + i) * a.KB + kb;
+      lds_load4(R.w, cs + CS::kHi + i * 256, i < nt ? bi * BLK + 1024 + lane * 4 : kNoLoad);
+    } else if (j < BL::kTiles + 2) {
+      // scale (or zero-point) words of the 2 NP tiles, szb bytes each, 16 bytes per lane by the
+      // lanes that cover them (at least 8 of the 64, whatever the group size)
+      const int szb = 4 * a.szw;
+      if (lane * 16 < 2 * NP * szb) {
+        const int i = lane * 16 / szb;
+        const int off = i < nt ? ((t0 + i) * a.KB + kb) * szb + lane * 16 % szb : kNoLoad;
+        if (j == BL::kTiles)
+          lds_load16(R.s, cs + CS::kS, off);
+        else
+          lds_load16(R.z, cs + CS::kZ, off);
+      }
+    } else {
+      const int r0 = 4 * (j - BL::kTiles - 2);
+      lds_load16(R.x, xs + r0 * 256, voff[(r0 & 15) >> 2] + (r0 * a.K + kb * 128) * 2);
+    }
+  }
+}
+
+// Steps of wave C among NC: with 4 waves, 2 consecutive 16-k steps (dwords J0, J0+1 of set S of
+// every pair's packed block); with 8, one.
 template <int NC, int C>
 struct Steps {
   static constexpr int kN = 8 / NC;
@@ -152,7 +211,7 @@ struct CodeWords<2> {
   static __device__ __forceinline__ uint32_t at(T v, int j) { return v[j]; }
 };
 
-// Operands of one block for one consumer, read from LDS one block ahead of the math.
+// Operands of one block for one wave, read from LDS one block ahead of the math.
 template <int BITS, int NP, int NTT, int N>
 struct Frag {
   typename CodeWords<N>::T cw[NP];
@@ -160,34 +219,38 @@ struct Frag {
   f16x8 B[N][NTT];
 };
 
-// One consumer (wave C): its steps of every block.  Iteration kb reads block kb + 1 (certified by
-// barrier B(kb)) into registers, then runs the math of block kb from the registers read in the
-// previous iteration, so the LDS latency hides behind a block of matrix-core work.
-template <int BITS, int NP, int NTT, int NC, int DC, int DX, int C, bool FAST>
-__device__ __forceinline__ void consume(const KArgs& a, const char* cring, const char* xring,
-                                        f32x16 (&acc)[NP][NTT]) {
+// Byte layout of one ring stage: the code part (CodeStage), then the activation tile.
+template <int BITS, int NP, int NTT>
+struct Stage {
+  static constexpr int kCode = CodeStage<BITS, NP>::kBytes;
+  static constexpr int kBytes = kCode + 32 * NTT * 256;
+};
+
+// Operand reads and math of math wave C: read() fills a register set from a block's code part
+// cs and activation tile xs; math() runs the wave's steps of that block.
+template <int BITS, int NP, int NTT, int NC, int C, bool FAST>
+struct WaveMath {
   using CS = CodeStage<BITS, NP>;
   using ST = Steps<NC, C>;
   using CWd = CodeWords<ST::kN>;
   using F = Frag<BITS, NP, NTT, ST::kN>;
-  constexpr int BN = 32 * NTT, XB = BN * 256;
-  const int lane = threadIdx.x & 63;
-  const LaneMap m = lane_map(a, lane);
-  const uint32_t magic = vgpr_const(0x64006400u);
-  const int brow = lane & 31;
-  const int bsw = brow * 256 + 16 * ((4 * (lane >> 5)) ^ (brow & 15));
-  const int slot = m.slot16[ST::kS];
-  // lane-constant byte offsets inside a code stage
-  const int lo_off = CS::kLo + m.th * 1024 + slot + 4 * ST::kJ0;
-  const int hi_off = CS::kHi + m.th * 256 + slot / 4;
-  const int szb = 4 * a.szw;  // bytes of one tile's scale (or zero-point) block
-  const int sz_off = m.th * szb + m.szoff;
-  const int KB = a.KB;
-  const bool half_last = (KB * 128 != a.K);  // last block holds one group only
+  uint32_t magic;
+  int bsw, lo_off, hi_off, szb, sz_off;
 
-  auto read = [&](int b, F& f) {
-    const char* cs = cring + (b % DC) * CS::kBytes;
-    const char* xs = xring + (b % DX) * XB;
+  __device__ __forceinline__ explicit WaveMath(const KArgs& a) {
+    const int lane = threadIdx.x & 63;
+    const LaneMap m = lane_map(a, lane);
+    magic = vgpr_const(0x64006400u);
+    const int brow = lane & 31;
+    bsw = brow * 256 + 16 * ((4 * (lane >> 5)) ^ (brow & 15));
+    const int slot = m.slot16[ST::kS];
+    // lane-constant byte offsets inside a code stage
+    lo_off = CS::kLo + m.th * 1024 + slot + 4 * ST::kJ0;
+    hi_off = CS::kHi + m.th * 256 + slot / 4;
+    szb = 4 * a.szw;  // bytes of one tile's scale (or zero-point) block
+    sz_off = m.th * szb + m.szoff;
+  }
+  __device__ __forceinline__ void read(const char* cs, const char* xs, F& f) const {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       f.cw[p] = *reinterpret_cast<const typename CWd::T*>(cs + lo_off + p * 2048);
@@ -197,8 +260,8 @@ __device__ __forceinline__ void consume(const KArgs& a, const char* cring, const
     }
     load_b<NTT, 2 * ST::kJ0 + ST::kS>(xs, bsw, f.B[0]);
     if constexpr (ST::kN == 2) load_b<NTT, 2 * (ST::kJ0 + 1) + ST::kS>(xs, bsw, f.B[ST::kN - 1]);
-  };
-  auto math = [&](const F& f) {
+  }
+  __device__ __forceinline__ void math(const F& f, f32x16 (&acc)[NP][NTT]) const {
 #pragma unroll
     for (int j = 0; j < ST::kN; ++j) {
 #pragma unroll
@@ -209,18 +272,32 @@ __device__ __forceinline__ void consume(const KArgs& a, const char* cring, const
         for (int tt = 0; tt < NTT; ++tt) acc[p][tt] = mfma32(A, f.B[j][tt], acc[p][tt]);
       }
     }
-  };
+  }
+  // the second step of waves with J0 = 2 falls in the missing group of a half-empty last block
+  static constexpr bool kSkipsHalfBlock = ST::kJ0 >= 2;
+};
 
+// Producer layout, math wave C.  Iteration kb: barrier B(kb) (block kb + 1 is in LDS; every
+// wave has finished reading block kb), read block kb + 1 into registers, then the math of block
+// kb from the registers read one iteration earlier, so the LDS latency hides behind a block of
+// matrix-core work.  (Barrier B(-1), block 0 in LDS, was passed by the caller.)
+template <int BITS, int NP, int NTT, int NC, int DC, int DX, int C, bool FAST>
+__device__ __forceinline__ void consume(const KArgs& a, const char* cring, const char* xring,
+                                        f32x16 (&acc)[NP][NTT]) {
+  using W = WaveMath<BITS, NP, NTT, NC, C, FAST>;
+  constexpr int XB = 32 * NTT * 256;
+  const W wm(a);
+  const int KB = a.KB;
+  const bool half_last = (KB * 128 != a.K);  // last block holds one group only
   // two register sets used in turn (no copies, so the reads of one set never wait for the
   // math of the other)
-  F f0, f1;
-  auto step = [&](int kb, F& mine, F& other) {
-    arrive_wait();  // B(kb): block kb + 1 is in LDS; everyone has finished reading block kb
-    if (kb + 1 < KB) read(kb + 1, other);
-    if (ST::kJ0 < 2 || !(half_last && kb == KB - 1)) math(mine);
+  typename W::F f0, f1;
+  auto step = [&](int kb, typename W::F& mine, typename W::F& other) {
+    arrive_wait();  // B(kb)
+    if (kb + 1 < KB) wm.read(cring + ((kb + 1) % DC) * W::CS::kBytes, xring + ((kb + 1) % DX) * XB, other);
+    if (!W::kSkipsHalfBlock || !(half_last && kb == KB - 1)) wm.math(mine, acc);
   };
-  // (barrier B(-1), block 0 in LDS, was passed by the caller)
-  read(0, f0);
+  wm.read(cring, xring, f0);
   int kb = 0;
   for (; kb + 1 < KB; kb += 2) {
     step(kb, f0, f1);
@@ -229,13 +306,84 @@ __device__ __forceinline__ void consume(const KArgs& a, const char* cring, const
   if (kb < KB) step(kb, f0, f1);
 }
 
-template <int BITS, int NP, int NTT, int NC, int DC, int DX, int C>
-__device__ __forceinline__ void consumer(const KArgs& a, const char* cring, const char* xring,
-                                         bool fast, f32x16 (&acc)[NP][NTT]) {
-  if (fast)
-    consume<BITS, NP, NTT, NC, DC, DX, C, true>(a, cring, xring, acc);
-  else
-    consume<BITS, NP, NTT, NC, DC, DX, C, false>(a, cring, xring, acc);
+// Self-loading layout, wave C.  Ring of D stages, block b in stage b % D.  Iteration kb: wait
+// until this wave's loads of block kb + 1 have landed, barrier B(kb) (block kb + 1 complete in
+// LDS; every wave has finished reading block kb), refill block kb's stage with block kb + D,
+// read block kb + 1 into registers, then the math of block kb.  Blocks 0 .. D-1 were issued
+// and barrier B(-1) passed before.
+template <int BITS, int NP, int NTT, int NC, int D, int C, bool FAST>
+__device__ __forceinline__ void run_wave(const KArgs& a, char* ring, const Rsrcs& R,
+                                         const int (&voff)[4], int t0, int nt,
+                                         f32x16 (&acc)[NP][NTT]) {
+  using W = WaveMath<BITS, NP, NTT, NC, C, FAST>;
+  using SG = Stage<BITS, NP, NTT>;
+  constexpr int BN = 32 * NTT;
+  constexpr int NWAIT = (D - 2) * BlockLoads<BITS, NP, BN>::per_wave(C, NC);
+  static_assert(D >= 2, "ring too shallow");
+  const W wm(a);
+  const int lane = threadIdx.x & 63;
+  const int KB = a.KB;
+  const bool half_last = (KB * 128 != a.K);
+  typename W::F f0, f1;
+  auto step = [&](int kb, typename W::F& mine, typename W::F& other) {
+    wait_vmcnt<NWAIT>();  // this wave's loads of block kb + 1
+    arrive_wait();        // B(kb)
+    char* st = ring + (kb % D) * SG::kBytes;
+    issue_block<BITS, NP, BN, NC, C>(R, a, st, st + SG::kCode, voff, t0, nt, min(kb + D, KB - 1), lane);
+    if (kb + 1 < KB) {
+      const char* cs = ring + ((kb + 1) % D) * SG::kBytes;
+      wm.read(cs, cs + SG::kCode, other);
+    }
+    if (!W::kSkipsHalfBlock || !(half_last && kb == KB - 1)) wm.math(mine, acc);
+  };
+  wm.read(ring, ring + SG::kCode, f0);
+  int kb = 0;
+  for (; kb + 1 < KB; kb += 2) {
+    step(kb, f0, f1);
+    step(kb + 1, f1, f0);
+  }
+  if (kb < KB) step(kb, f0, f1);
+}
+
+// Self-loading layout: wave C's share of blocks 0 .. D-1.
+template <int BITS, int NP, int NTT, int NC, int D, int C>
+__device__ __forceinline__ void prologue(const KArgs& a, char* ring, const Rsrcs& R,
+                                         const int (&voff)[4], int t0, int nt) {
+  using SG = Stage<BITS, NP, NTT>;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    issue_block<BITS, NP, 32 * NTT, NC, C>(R, a, ring + j * SG::kBytes, ring + j * SG::kBytes + SG::kCode,
+                                           voff, t0, nt, min(j, a.KB - 1), lane);
+}
+
+// Math wave C of either layout: (self-loading) wait for its share of block 0 and pass B(-1)
+// (producer layout: passed by the caller), read the zero-point votes, then the main loop with
+// the dequantisation they select.
+template <int BITS, int NP, int NTT, bool SELF, int D1, int D2, int C>
+__device__ __forceinline__ void math_wave(const KArgs& a, char* smem, const Rsrcs& R,
+                                          const int (&voff)[4], int t0, int nt, const int* votes,
+                                          f32x16 (&acc)[NP][NTT]) {
+  constexpr int NC = 4;
+  if constexpr (SELF) {
+    wait_vmcnt<(D1 - 1) * BlockLoads<BITS, NP, 32 * NTT>::per_wave(C, NC)>();
+    arrive_wait();  // B(-1)
+  }
+  bool fast = true;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) fast = fast && votes[c] != 0;
+  if constexpr (SELF) {
+    if (fast)
+      run_wave<BITS, NP, NTT, NC, D1, C, true>(a, smem, R, voff, t0, nt, acc);
+    else
+      run_wave<BITS, NP, NTT, NC, D1, C, false>(a, smem, R, voff, t0, nt, acc);
+  } else {
+    char* const xring = smem + D1 * CodeStage<BITS, NP>::kBytes;
+    if (fast)
+      consume<BITS, NP, NTT, NC, D1, D2, C, true>(a, smem, xring, acc);
+    else
+      consume<BITS, NP, NTT, NC, D1, D2, C, false>(a, smem, xring, acc);
+  }
 }
 
 // Rows of each workgroup: units of `ut` tiles (1, or 2 for the SwiGLU pair, whose gate and up
@@ -246,11 +394,15 @@ struct Part {
   int units, ut, chunk;
 };
 
-// Workgroup = NC consumer waves (math) + 1 code producer + 1 activation producer.  LDS: the code
-// ring (DC stages), then the activation ring (DX stages); the reduction at the end reuses it.
-template <int BITS, int NP, int NTT, int NC, int DC, int DX, int EPI>
-__global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a, Part part) {
+// Workgroup: 4 math waves, plus (producer layout) a code producer and an activation producer.
+// LDS, producer layout: the code ring (D1 = DC stages), the activation ring (D2 = DX stages);
+// self-loading layout: the ring of D1 stages.  The zero-point votes sit past the ring(s); the
+// reduction at the end reuses all of it.
+template <int BITS, int NP, int NTT, bool SELF, int D1, int D2, int EPI>
+__global__ __launch_bounds__(SELF ? 256 : 384) void narrow_kernel(KArgs a, Part part) {
   using CS = CodeStage<BITS, NP>;
+  using SG = Stage<BITS, NP, NTT>;
+  constexpr int NC = 4;
   constexpr int BN = 32 * NTT, XB = BN * 256;
   // token block blockIdx.y: tokens BN y .. BN y + BN - 1 (more than one only when T > BN)
   if (blockIdx.y > 0) {
@@ -263,9 +415,8 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a, Part par
   }
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const cring = smem;
-  char* const xring = smem + DC * CS::kBytes;
-  // the zero-point votes sit past both rings (the reduction at the end may reuse them)
-  int* const votes = reinterpret_cast<int*>(xring + DX * XB);
+  char* const xring = smem + D1 * CS::kBytes;  // (producer layout)
+  int* const votes = reinterpret_cast<int*>(SELF ? smem + D1 * SG::kBytes : xring + D2 * XB);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ntiles = a.rows / 16;
@@ -294,36 +445,58 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a, Part par
     voff[i] = (rl * a.K + ((lane & 15) ^ (4 * i + rl)) * 8) * 2;
   }
 
-  // Producers start streaming at once; the consumers vote on the zero-points meanwhile: are all
-  // of this workgroup's zero-points integers (1024 + z exact in fp16)?  The votes meet in LDS
-  // at barrier B(-1), which the producers reach as soon as their first block has landed (a
-  // fenced barrier here would hold them until their whole prologue had).
-  if (wave == NC) {
+  // Producer layout: the producers start streaming at once, the math waves vote on the
+  // zero-points meanwhile (are all of this workgroup's zero-points integers, 1024 + z exact in
+  // fp16?), and the votes meet in LDS at barrier B(-1), which the producers reach as soon as
+  // their first block has landed.  Self-loading layout: each wave's first vote loads go out
+  // ahead of its share of the prologue, so that the vote waits only for its own loads (later
+  // passes, past 64 KB of zero-points, wait behind the prologue).  Past the last tile the range
+  // check reads zeros (integers).
+  if (!SELF && wave >= NC) {
+    if constexpr (!SELF) {
+      if (wave == NC) {
 #pragma unroll
-    for (int j = 0; j < DC; ++j)
-      load_codes<BITS, NP>(R, a, cring + j * CS::kBytes, t0, nt, min(j, KB - 1), lane);
-  } else if (wave == NC + 1) {
+        for (int j = 0; j < D1; ++j)
+          load_codes<BITS, NP>(R, a, cring + j * CS::kBytes, t0, nt, min(j, KB - 1), lane);
+      } else {
 #pragma unroll
-    for (int j = 0; j < DX; ++j) load_x<BN>(R, a, xring + j * XB, voff, min(j, KB - 1));
+        for (int j = 0; j < D2; ++j) load_x<BN>(R, a, xring + j * XB, voff, min(j, KB - 1));
+      }
+    }
   } else {
     const int zbase = t0 * KB * 4 * a.szw;  // bytes: zero-points of the workgroup's tiles
     const int zbytes = nt * KB * 4 * a.szw;
     const f16x2 c1024 = {(f16)1024.0f, (f16)1024.0f};
-    constexpr int STEP = 64 * NC * 16;  // bytes per load instruction of all consumers
+    constexpr int STEP = 64 * NC * 16;  // bytes per load instruction of the four math waves
     bool exact = true;
-    for (int off0 = threadIdx.x * 16; off0 < zbytes; off0 += 4 * STEP) {
-      // four loads in flight per pass (one pass up to K = 8192 with two pairs); past the last
-      // tile the range check reads zeros (integers)
-      u32x4 zz[4];
+    auto pass_load = [&](int off0, u32x4 (&zz)[4]) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         zz[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(R.z, zbase + off0 + u * STEP, 0, 0));
+    };
+    auto pass_check = [&](int off0, const u32x4 (&zz)[4]) {
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           exact = exact && (off0 + u * STEP >= zbytes ||
                             __builtin_bit_cast(uint32_t, (as_h2(zz[u][e]) + c1024) - c1024) == zz[u][e]);
+    };
+    int off0 = threadIdx.x * 16;
+    u32x4 zz[4];
+    pass_load(off0, zz);
+    if constexpr (SELF) {
+      switch (wave) {
+        case 0: prologue<BITS, NP, NTT, NC, D1, 0>(a, smem, R, voff, t0, nt); break;
+        case 1: prologue<BITS, NP, NTT, NC, D1, 1>(a, smem, R, voff, t0, nt); break;
+        case 2: prologue<BITS, NP, NTT, NC, D1, 2>(a, smem, R, voff, t0, nt); break;
+        default: prologue<BITS, NP, NTT, NC, D1, 3>(a, smem, R, voff, t0, nt); break;
+      }
+    }
+    pass_check(off0, zz);
+    for (off0 += 4 * STEP; off0 < zbytes; off0 += 4 * STEP) {
+      pass_load(off0, zz);
+      pass_check(off0, zz);
     }
     const bool all = __ballot(exact) == ~0ull;
     if (lane == 0) votes[wave] = all ? 1 : 0;
@@ -335,45 +508,27 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a, Part par
 #pragma unroll
     for (int tt = 0; tt < NTT; ++tt) acc[p][tt] = f32x16{};
 
-  if (wave < NC) {
-    arrive_wait();  // B(-1): block 0 is in LDS, and so are the votes
-  }
-  bool fast = true;
-#pragma unroll
-  for (int c = 0; c < NC; ++c) fast = fast && (wave >= NC || votes[c] != 0);
-
-  if (wave == NC) {
-    produce<DC, CS::kOps>(KB, [&](int st, int kb) {
-      load_codes<BITS, NP>(R, a, cring + st * CS::kBytes, t0, nt, kb, lane);
-    });
-  } else if (wave == NC + 1) {
-    produce<DX, BN / 4>(KB, [&](int st, int kb) { load_x<BN>(R, a, xring + st * XB, voff, kb); });
-  } else {
-#define W4_CONSUMER(C)                                                             \
-  case C:                                                                          \
-    consumer<BITS, NP, NTT, NC, DC, DX, C>(a, cring, xring, fast, acc); \
-    break;
-    switch (wave) {
-      W4_CONSUMER(0)
-      W4_CONSUMER(1)
-      W4_CONSUMER(2)
-      W4_CONSUMER(3)
-      default:
-        if constexpr (NC == 8) {
-          switch (wave) {
-            W4_CONSUMER(4)
-            W4_CONSUMER(5)
-            W4_CONSUMER(6)
-            default: consumer<BITS, NP, NTT, NC, DC, DX, 7>(a, cring, xring, fast, acc); break;
-          }
-        }
-        break;
+  if (!SELF && wave >= NC) {
+    if constexpr (!SELF) {
+      if (wave == NC)
+        produce<D1, CS::kOps>(KB, [&](int st, int kb) {
+          load_codes<BITS, NP>(R, a, cring + st * CS::kBytes, t0, nt, kb, lane);
+        });
+      else
+        produce<D2, BN / 4>(KB, [&](int st, int kb) { load_x<BN>(R, a, xring + st * XB, voff, kb); });
     }
-#undef W4_CONSUMER
+  } else {
+    if constexpr (!SELF) arrive_wait();  // B(-1): block 0 is in LDS, and so are the votes
+    switch (wave) {
+      case 0: math_wave<BITS, NP, NTT, SELF, D1, D2, 0>(a, smem, R, voff, t0, nt, votes, acc); break;
+      case 1: math_wave<BITS, NP, NTT, SELF, D1, D2, 1>(a, smem, R, voff, t0, nt, votes, acc); break;
+      case 2: math_wave<BITS, NP, NTT, SELF, D1, D2, 2>(a, smem, R, voff, t0, nt, votes, acc); break;
+      default: math_wave<BITS, NP, NTT, SELF, D1, D2, 3>(a, smem, R, voff, t0, nt, votes, acc); break;
+    }
   }
 
-  // Drain the producers' tail loads (they target LDS reused below), then add the NC partial
-  // sums in wave order.  red[w][p][tt][v][lane].
+  // Drain the tail loads (they target LDS reused below), then add the four partial sums in wave
+  // order.  red[w][p][tt][v][lane].
   wait_vmcnt<0>();
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
@@ -418,24 +573,33 @@ __global__ __launch_bounds__(64 * (NC + 2)) void narrow_kernel(KArgs a, Part par
   }
 }
 
-template <int BITS, int NP, int NTT, int EPI>
+// Producer layout: code ring as deep as the code producer's load counter allows (at most 12),
+// activation ring likewise for the activation producer.  Self-loading layout: as many stages as
+// the LDS holds, within each wave's load counter, at most 16.
+template <int BITS, int NP, int NTT, bool SELF, int EPI>
 hipError_t run(const KArgs& a, int grid, Part part, hipStream_t stream) {
   using CS = CodeStage<BITS, NP>;
+  using SG = Stage<BITS, NP, NTT>;
+  constexpr int NC = 4;
   constexpr int BN = 32 * NTT;
-  constexpr int NC = 4;  // consumer waves
-  // activation stages: as deep as the activation producer's load counter allows (its loads
-  // share the memory queues with the weight stream, so they see its latency)
-  constexpr int DX = 63 / (BN / 4) + 1;
+  constexpr int kLds = 160 * 1024;
   constexpr int DCMAX = 63 / CS::kOps + 1;
-  constexpr int DC = DCMAX < 12 ? DCMAX : 12;  // code stages
-  constexpr size_t rings = (size_t)DC * CS::kBytes + (size_t)DX * BN * 256 + NC * sizeof(int);
+  constexpr int DX = 63 / (BN / 4) + 1;
+  constexpr int NMAX = BlockLoads<BITS, NP, BN>::per_wave(0, NC);
+  constexpr int D_LDS = (kLds - NC * (int)sizeof(int)) / SG::kBytes;
+  constexpr int D_CNT = 63 / NMAX + 1;
+  constexpr int D_SELF = D_LDS < D_CNT ? (D_LDS < 16 ? D_LDS : 16) : (D_CNT < 16 ? D_CNT : 16);
+  constexpr int D1 = SELF ? D_SELF : (DCMAX < 12 ? DCMAX : 12);
+  constexpr int D2 = SELF ? 0 : DX;
+  constexpr size_t rings = SELF ? (size_t)D1 * SG::kBytes + NC * sizeof(int)
+                                : (size_t)D1 * CS::kBytes + (size_t)D2 * BN * 256 + NC * sizeof(int);
   constexpr size_t red = (size_t)NC * NP * NTT * 16 * 64 * 4;
   constexpr size_t lds = rings > red ? rings : red;
-  static_assert(lds <= 160 * 1024, "LDS of one workgroup");
+  static_assert(lds <= kLds, "LDS of one workgroup");
   const int ntb = (a.T + BN - 1) / BN;
   if (ntb > 65535) return hipErrorInvalidConfiguration;  // grid y limit (T above 4 million)
-  return launch_kernel(&narrow_kernel<BITS, NP, NTT, NC, DC, DX, EPI>, dim3(grid, ntb),
-                       dim3(64 * (NC + 2)), lds, stream, a, part);
+  return launch_kernel(&narrow_kernel<BITS, NP, NTT, SELF, D1, D2, EPI>, dim3(grid, ntb),
+                       dim3(SELF ? 256 : 384), lds, stream, a, part);
 }
 
 constexpr int kCUs = 256;    // compute units of the chip (gfx950, MI350 series)
@@ -451,8 +615,8 @@ hipError_t pick_np(bool balanced, const KArgs& a, hipStream_t stream) {
     const int np = npairs >= 2 * 160 ? 2 : 1;
     const int grid = (npairs + np - 1) / np;
     const Part part{npairs, 2, np};
-    return np == 2 ? run<BITS, 2, NTT, EPI>(a, grid, part, stream)
-                   : run<BITS, 1, NTT, EPI>(a, grid, part, stream);
+    return np == 2 ? run<BITS, 2, NTT, false, EPI>(a, grid, part, stream)
+                   : run<BITS, 1, NTT, false, EPI>(a, grid, part, stream);
   }
   // Balanced: one workgroup per compute unit (fewer when there are fewer units), each with an
   // even share of the units; more workgroups only when a share would exceed kMaxPairs pairs.
@@ -464,12 +628,18 @@ hipError_t pick_np(bool balanced, const KArgs& a, hipStream_t stream) {
   const int per = (units + grid - 1) / grid;  // largest share
   const int np = (per * ut + 1) / 2;
   const Part part{units, ut, 0};
+  // Layout: self-loading for 64-token tiles over three or more pairs (the SwiGLU pair at
+  // 17408 x 2 rows, T = 64: 45.1 against 51.7 us with producer waves, whose five-pair 64-token
+  // instance spills); producer waves otherwise, where a block's activation tile is large against
+  // its codes (one or two pairs) or the 32-token instances fit anyway (T = 32: 31.7 against
+  // 34.2 us self-loading).
+  constexpr bool kSelf = NTT == 2;
   switch (np) {
-    case 1: return run<BITS, 1, NTT, EPI>(a, grid, part, stream);
-    case 2: return run<BITS, 2, NTT, EPI>(a, grid, part, stream);
-    case 3: return run<BITS, 3, NTT, EPI>(a, grid, part, stream);
-    case 4: return run<BITS, 4, NTT, EPI>(a, grid, part, stream);
-    default: return run<BITS, 5, NTT, EPI>(a, grid, part, stream);
+    case 1: return run<BITS, 1, NTT, false, EPI>(a, grid, part, stream);
+    case 2: return run<BITS, 2, NTT, false, EPI>(a, grid, part, stream);
+    case 3: return run<BITS, 3, NTT, kSelf, EPI>(a, grid, part, stream);
+    case 4: return run<BITS, 4, NTT, kSelf, EPI>(a, grid, part, stream);
+    default: return run<BITS, 5, NTT, kSelf, EPI>(a, grid, part, stream);
   }
 }
 

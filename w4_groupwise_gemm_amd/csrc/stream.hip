@@ -300,7 +300,8 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx, ch
     for (int i = 0; i < KPW; ++i) {
       // (ring modes issue every slot, re-reading a wave's last block past its end, so that the
       // tile waits below can count the loads issued after each tile)
-      if (i + D < KPW && (RING || i + D < nb)) issue(i + D);
+      // (the two-slot ring issues its code loads with its tile refills, below)
+      if (NSLOT != 2 && i + D < KPW && (RING || i + D < nb)) issue(i + D);
       if (i < nb) {
         const int kb = wave + NW * (cb + i);
         const bool half_block = HB && (kb * 128 + 64 >= a.K);
@@ -309,19 +310,22 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx, ch
         f16x8 Bf[4], Bx[TH > 1 ? TH - 1 : 1][4];
         if constexpr (RING) {
           // The ring tile of block i has landed once at most the loads issued after it are
-          // outstanding.  Issue order: tiles 0 (and 1 with two slots), code blocks 0 .. D-1;
-          // then code block i + D at the top of block i; the refill of tile i + 2 after block
-          // i's math (two slots) or of tile i + 1 right after block i's tile has been read (one
-          // slot).  CPB: code loads per block.
+          // outstanding.  CPB: code loads per block.
+          //  * Two slots: tiles 0 and 1, code blocks 0 .. D-1 (D = 2); after block i's math the
+          //    refill of tile i + 2, then code block i + 2.  A code block thus follows every
+          //    tile load issued before its own block's tile, so the compiler's wait for its
+          //    registers (which counts only register loads) waits for at most the next block's
+          //    tile besides, never for later code blocks.
+          //  * One slot: tile 0, code blocks 0 .. D-1; then code block i + D at the top of
+          //    block i, and the refill of tile i + 1 right after block i's tile has been read.
           constexpr int CPB = RT * (BITS == 5 ? 4 : 3);
-          const int first = CPB * (D + (D < KPW ? 1 : 0));  // codes issued before block 0's wait
           int n;
           if constexpr (NSLOT == 2)
-            n = i == 0 ? first
-              : i == 1 ? 63  // (tile 1 was waited for with tile 0)
-              : CPB * (i - 1 + D < KPW) + 8 * (i + 1 < KPW) + CPB * (i + D < KPW);
+            n = i == 0 ? 8 + D * CPB
+              : i == 1 ? D * CPB + (2 < KPW ? 8 + CPB : 0)
+              : CPB + (i + 1 < KPW ? 8 + CPB : 0);
           else
-            n = i == 0 ? first : CPB * (i + D < KPW);
+            n = i == 0 ? CPB * (D + (D < KPW ? 1 : 0)) : CPB * (i + D < KPW);
           wait_vmcnt_folded(n);
         }
         if constexpr (MODE == MODE_MFMA) {
@@ -424,9 +428,12 @@ __device__ __forceinline__ void stream_body(const KArgs& a, int xdim, int bx, ch
       }
       if constexpr (XL == 32) {
         if (i + 2 < KPW) {
-          // this wave's reads of slot i % 2 are complete: refill it with block i + 2's tile
+          // this wave's reads of slot i % 2 are complete: refill it with block i + 2's tile,
+          // then issue block i + 2's codes
           __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt 0 (vmcnt, expcnt: no wait)
           xload(i + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          issue(i + 2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -616,7 +623,7 @@ inline int tiles_per_workgroup(int ntiles, int bits, int max_rt, int start) {
 
 template <int RT, int XL, int KPW>
 constexpr int ring_depth() {
-  constexpr int d = XL >= 32 ? 5 : XL >= 8 ? (RT >= 6 ? 2 : 5) : RT >= 2 ? 2 : (XL ? 5 : 3);
+  constexpr int d = XL == 32 ? 2 : XL >= 32 ? 5 : XL >= 8 ? (RT >= 6 ? 2 : 5) : RT >= 2 ? 2 : (XL ? 5 : 3);
   return d < KPW ? d : KPW;
 }
 

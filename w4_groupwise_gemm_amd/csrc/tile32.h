@@ -116,10 +116,18 @@ __device__ __forceinline__ void load_x_lds(const Rsrcs& R, const KArgs& a, char*
   }
 }
 
-// B lane l of step (J, S): token row 32 tt + l%32, k = 64 (J/2) + 16 (S + 2 h) + 8 (J%2) + e,
+// B lane l of step (J, S) = step I = 2 J + S, token tile tt: token row 32 tt + l%32,
+// k = 64 (J/2) + 16 (S + 2 h) + 8 (J%2) + e,
 // i.e. LDS chunk c = 8 (J/2) + (J%2) + 2 S + 4 h stored at c ^ (row & 15).  With
 // bsw = row * 256 + 16 ((4 h) ^ (row & 15)) and the constant part of c disjoint from 4 h in
 // bits, the slot is bsw ^ 16 C.
+template <int I>
+__device__ __forceinline__ f16x8 load_b1(const char* xs, int bsw, int tt) {
+  constexpr int J = I >> 1, S = I & 1;
+  constexpr int C = 8 * (J >> 1) + (J & 1) + 2 * S;
+  return *reinterpret_cast<const f16x8*>(xs + (bsw ^ (16 * C)) + tt * 32 * 256);
+}
+// The same for NTT token tiles.
 template <int NTT, int I>
 __device__ __forceinline__ void load_b(const char* xs, int bsw, f16x8 (&B)[NTT]) {
   constexpr int J = I >> 1, S = I & 1;

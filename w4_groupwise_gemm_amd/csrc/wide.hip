@@ -83,27 +83,25 @@ __device__ __forceinline__ void deq_a(const PairCodes<BITS>& cur, const ShareCod
     A4 = wfrag<BITS, J, FAST>(sh.cw[J & 1], sh.hw, magic, sh.zp, sh.sp);
 }
 
-// Step I of the software pipeline: the matrix-core steps of step I run while the B fragments of
-// step I + 1 are read and its A fragments dequantised.  The instruction order inside a step is
-// left to the compiler (measured: forcing one matrix-core step / one LDS read / a few vector ops
-// in turn was 4-6% slower); the barrier at the end keeps steps from mixing.
+// Step I of the software pipeline: the matrix-core steps of step I run while the A fragments of
+// step I + 1 are dequantised and its B fragments read, each into the register of token tile tt
+// as soon as step I's steps have taken it (one B set: the registers this frees keep the
+// five-pair instance from spilling).  The instruction order inside a step is otherwise left to
+// the compiler (measured: forcing one matrix-core step / one LDS read / a few vector ops in turn
+// was 4-6% slower); the barrier at the end keeps steps from mixing.
 template <int BITS, int NP, int NTT, int W, int I, bool FAST>
 __device__ __forceinline__ void wide_step(const PairCodes<BITS>& cur, const ShareCodes<BITS>& sh,
                                           const char* xs, int bsw, uint32_t magic,
                                           const f16x8& Acur, f16x8& Anxt, f16x8& A4,
-                                          const f16x8 (&Bcur)[NTT], f16x8 (&Bnxt)[NTT],
-                                          f32x16 (&acc)[NTT], f32x16 (&accs)[NTT]) {
+                                          f16x8 (&B)[NTT], f32x16 (&acc)[NTT], f32x16 (&accs)[NTT]) {
   constexpr bool SH = share_step<NP, W, I>();
   const f16x8 A4cur = A4;
-  if constexpr (I + 1 < 8) {
-    load_b<NTT, I + 1>(xs, bsw, Bnxt);
-    deq_a<BITS, NP, W, I + 1, FAST>(cur, sh, magic, Anxt, A4);
-  }
+  if constexpr (I + 1 < 8) deq_a<BITS, NP, W, I + 1, FAST>(cur, sh, magic, Anxt, A4);
 #pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) acc[tt] = mfma32(Acur, Bcur[tt], acc[tt]);
-  if constexpr (SH) {
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) accs[tt] = mfma32(A4cur, Bcur[tt], accs[tt]);
+  for (int tt = 0; tt < NTT; ++tt) {
+    acc[tt] = mfma32(Acur, B[tt], acc[tt]);
+    if constexpr (SH) accs[tt] = mfma32(A4cur, B[tt], accs[tt]);
+    if constexpr (I + 1 < 8) B[tt] = load_b1<I + 1>(xs, bsw, tt);
   }
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -118,7 +116,7 @@ __device__ __forceinline__ void wide_loop(const Rsrcs& R, const KArgs& a, char* 
   PairCodes<BITS> nxt;
   ShareCodes<BITS> sh{}, shn;
   if constexpr (NP == 5) load_share<BITS, W>(sh, R, a, m, spair, ntiles, 0);
-  f16x8 A0, A1, A4, B0[NTT], B1[NTT];
+  f16x8 A0, A1, A4, B[NTT];
   for (int kb = 0; kb < a.KB; ++kb) {
     // everything this wave issued has landed (its share of X(kb), the codes of block kb) ...
     wait_vmcnt<0>();
@@ -131,19 +129,19 @@ __device__ __forceinline__ void wide_loop(const Rsrcs& R, const KArgs& a, char* 
       if constexpr (NP == 5) load_share<BITS, W>(shn, R, a, m, spair, ntiles, kb + 1);
     }
     const char* xs = xbase + (kb & 1) * (BN * 256);
-    load_b<NTT, 0>(xs, bsw, B0);
+    load_b<NTT, 0>(xs, bsw, B);
     deq_a<BITS, NP, W, 0, FAST>(cur, sh, magic, A0, A4);
-    wide_step<BITS, NP, NTT, W, 0, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B0, B1, acc, accs);
-    wide_step<BITS, NP, NTT, W, 1, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B1, B0, acc, accs);
-    wide_step<BITS, NP, NTT, W, 2, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B0, B1, acc, accs);
+    wide_step<BITS, NP, NTT, W, 0, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B, acc, accs);
+    wide_step<BITS, NP, NTT, W, 1, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B, acc, accs);
+    wide_step<BITS, NP, NTT, W, 2, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B, acc, accs);
     // (step 3 also prepares step 4; in a half-empty block that reads LDS and codes that exist
     // but are never used)
-    wide_step<BITS, NP, NTT, W, 3, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B1, B0, acc, accs);
+    wide_step<BITS, NP, NTT, W, 3, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B, acc, accs);
     if (kb * 128 + 64 < a.K) {
-      wide_step<BITS, NP, NTT, W, 4, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B0, B1, acc, accs);
-      wide_step<BITS, NP, NTT, W, 5, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B1, B0, acc, accs);
-      wide_step<BITS, NP, NTT, W, 6, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B0, B1, acc, accs);
-      wide_step<BITS, NP, NTT, W, 7, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B1, B0, acc, accs);
+      wide_step<BITS, NP, NTT, W, 4, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B, acc, accs);
+      wide_step<BITS, NP, NTT, W, 5, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B, acc, accs);
+      wide_step<BITS, NP, NTT, W, 6, FAST>(cur, sh, xs, bsw, magic, A0, A1, A4, B, acc, accs);
+      wide_step<BITS, NP, NTT, W, 7, FAST>(cur, sh, xs, bsw, magic, A1, A0, A4, B, acc, accs);
     }
     if (more) {
       cur = nxt;

@@ -68,6 +68,9 @@ def test_route_table_domains_cover_every_width():
     (0, 5, 4, 6144, "mfma_stream_t16"), (0, 5, 5, 6144, "mfma_splitk_t32"),
     (2, 4, 20, 17408, "mfma_splitk_t32"), (0, 4, 21, 8192, "mfma_narrow_t32"),
     (0, 5, 64, 12288, "mfma_narrow_t64"),
+    # 5-bit codes leave split K earlier: at 15 tokens for K = 6144, at 18 beyond
+    (2, 5, 14, 6144, "mfma_splitk_t32"), (2, 5, 15, 6144, "mfma_narrow_t32"),
+    (0, 5, 17, 8192, "mfma_splitk_t32"), (0, 5, 18, 17408, "mfma_narrow_t32"),
     # the SwiGLU pair at K > 5120 never takes split K
     (1, 5, 16, 6144, "mfma_stream_t16"), (1, 5, 17, 6144, "mfma_narrow_t32"),
 ])

@@ -137,10 +137,10 @@ int pick_route(int op, int bits, int T, int N, int K) {
   //    13.1 against 23.3); for 17-32 tokens its 32-row ring leads (T = 32: 13.2 against 15.8
   //    for the narrow kernel, 5-bit 15.1 against 18.0; SwiGLU pair 44.4 against 45.7).
   //  * K > 5120: beyond 4 tokens the streaming route's activation fragments ride in its load
-  //    ring and split K leads to T = 20 (6144 / 8192 / 12288 / 17408 columns at T = 16, 5-bit:
-  //    15.0 / 16.8 / 23.4 / 31.5 against 18.4 / 21.2 / 30.7 / 43.7 streamed and 15.5 / 18.6 /
-  //    25.7 / 35.1 narrow); from T = 24 the narrow kernel leads (15.6 / 18.7 / 25.7 / 34.9
-  //    against 16.5 / 19.4 / 27.4 / 37.3).  The SwiGLU pair streams two row tiles per
+  //    ring and split K leads (8192 / 12288 / 17408 columns at T = 16, 5-bit: 16.8 / 23.3 /
+  //    31.4 against 21.2 / 30.5 / 43.6 streamed and 17.4 / 23.8 / 32.3 narrow) to 20 tokens
+  //    with 4-bit codes and to 17 with 5-bit codes (14 at 6144 columns), after which the
+  //    narrow kernel leads (boundaries below).  The SwiGLU pair streams two row tiles per
   //    workgroup, which keeps the streaming route ahead up to 16 tokens, and the narrow kernel
   //    after that (split K: 41.7 against 32.1 streamed at T = 16, 44.0 against 42.9 narrow at 20).
   //  * 33-64 tokens: the streaming kernel's one-slot 64-row ring is ahead for single 4-bit
@@ -167,8 +167,13 @@ int pick_route(int op, int bits, int T, int N, int K) {
     if (T <= 32) return R_N32;
     if (T <= 64) return R_N64;
   } else {
+    // split K to 20 tokens with 4-bit codes; with 5-bit codes (more vector work per weight byte)
+    // the narrow kernel catches up earlier, at 15 tokens for K = 6144 and 18 beyond (T = 16 at
+    // 6144 columns: 14.5 against 15.1 us; T = 17 / 20 at 8192: 17.2 / 18.2 split against 17.5 /
+    // 17.6; 4-bit 8192 at T = 20: 16.2 against 17.2, at 24: 17.7 against 17.3)
     if (T <= 4) return R_N16;
-    if (T <= 20) return R_SPLITK;
+    const int split_max = bits == 4 ? 20 : K <= 6144 ? 14 : 17;
+    if (T <= split_max) return R_SPLITK;
     if (T <= 32) return R_N32;
     if (T <= 64) return R_N64;
   }

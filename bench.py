@@ -63,6 +63,8 @@ WORKLOADS = {
     "q5_k8192": ("q5_k8192", (1, 64), "linear"),
     "q5_k12288": ("q5_k12288", (1, 64), "linear"),
     "q4_k8192": ("q4_k8192", (1, 64), "linear"),
+    "swiglu_4096": ("swiglu_4096", (1, 64), "swiglu"),
+    "swiglu_q5_8192": ("swiglu_q5_8192", (1, 64), "swiglu"),
 }
 ALL_ORDER = ("decode", "tiny", "batched", "swiglu", "prefill")
 METRIC = "W4 GEMM effective weight GB/s (T<=64) and MFMA TFLOP/s (T>=1024), % roofline"

@@ -97,6 +97,16 @@ CONFIGS: Dict[str, dict] = {
     "q4_k17408": dict(
         mats=[("w", 5120, 17408)], bits=4, zero=("uniform", 6, 9), scale=(0.005, 0.02),
         x_sigma=1.0, outliers=8, Ts=(1, 64), op="linear"),
+    # SwiGLU pairs smaller than the measured one: a 4096-row 4-bit pair and an 8192-row 5-bit
+    # pair at K = 5120 (route-boundary sweeps only)
+    "swiglu_4096": dict(
+        mats=[("gate", 4096, 5120), ("up", 4096, 5120)], bits=4,
+        zero=("uniform", 6, 9), scale=(0.005, 0.02),
+        x_sigma=0.5, outliers=0, Ts=(1, 64), op="swiglu"),
+    "swiglu_q5_8192": dict(
+        mats=[("gate", 8192, 5120), ("up", 8192, 5120)], bits=5,
+        zero=("const", 16), scale=(0.0025, 0.01),
+        x_sigma=0.5, outliers=0, Ts=(1, 64), op="swiglu"),
 }
 
 OUTLIER_FACTOR = 30.0

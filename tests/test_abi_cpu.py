@@ -55,27 +55,35 @@ def test_route_table_domains_cover_every_width():
                     assert lo <= T <= hi, (op, bits, T, K, r)
 
 
-@pytest.mark.parametrize("op,bits,T,K,route", [
-    # K <= 5120: streaming to 16 tokens, its 32-row ring to 32, then the 64-row ring for 4-bit
-    # single matrices and the narrow kernel for 5-bit codes; the SwiGLU pair streams to 8
-    # tokens and takes the evenly spread narrow kernel beyond
-    (0, 4, 16, 5120, "mfma_stream_t16"), (0, 5, 17, 5120, "mfma_stream_t32"),
-    (2, 4, 64, 5120, "mfma_stream_t64"), (0, 5, 33, 5120, "mfma_narrow_t64"),
-    (1, 4, 8, 5120, "mfma_stream_t16"), (1, 4, 9, 5120, "mfma_bal_t32"),
-    (1, 4, 32, 5120, "mfma_bal_t32"), (1, 4, 33, 5120, "mfma_bal_t64"),
-    (1, 4, 64, 5120, "mfma_bal_t64"),
-    # K > 5120: streaming to 4 tokens, split K to 20, narrow beyond
-    (0, 5, 4, 6144, "mfma_stream_t16"), (0, 5, 5, 6144, "mfma_splitk_t32"),
-    (2, 4, 20, 17408, "mfma_splitk_t32"), (0, 4, 21, 8192, "mfma_narrow_t32"),
-    (0, 5, 64, 12288, "mfma_narrow_t64"),
-    # 5-bit codes leave split K earlier: at 15 tokens for K = 6144, at 18 beyond
-    (2, 5, 14, 6144, "mfma_splitk_t32"), (2, 5, 15, 6144, "mfma_narrow_t32"),
-    (0, 5, 17, 8192, "mfma_splitk_t32"), (0, 5, 18, 17408, "mfma_narrow_t32"),
-    # the SwiGLU pair at K > 5120 never takes split K
-    (1, 5, 16, 6144, "mfma_stream_t16"), (1, 5, 17, 6144, "mfma_narrow_t32"),
+@pytest.mark.parametrize("op,bits,T,N,K,route", [
+    # K <= 5120, single matrices: streaming to 16 tokens, its 32-row ring to 32, its 64-row ring
+    # to 64 (4-bit); 5-bit codes take the register ring at 5-16 and 33-48 tokens
+    (0, 4, 16, 12288, 5120, "mfma_stream_t16"), (0, 4, 17, 12288, 5120, "mfma_stream_t32"),
+    (2, 4, 64, 12288, 5120, "mfma_stream_t64"), (0, 5, 4, 12288, 5120, "mfma_stream_t16"),
+    (0, 5, 5, 12288, 5120, "mfma_reg_t16"), (0, 5, 16, 12288, 5120, "mfma_reg_t16"),
+    (0, 5, 17, 12288, 5120, "mfma_stream_t32"), (0, 5, 33, 12288, 5120, "mfma_reg_t64"),
+    (0, 5, 48, 12288, 5120, "mfma_reg_t64"), (0, 5, 49, 12288, 5120, "mfma_narrow_t64"),
+    # the SwiGLU pair at K <= 5120: streaming throughout with at most one pair per compute unit;
+    # otherwise streaming to 8 tokens, then the register ring (its 32-token instance from 9
+    # tokens with three or more pairs per compute unit)
+    (1, 4, 16, 4096, 5120, "mfma_stream_t16"), (1, 4, 32, 4096, 5120, "mfma_stream_t32"),
+    (1, 4, 64, 4096, 5120, "mfma_stream_t64"), (1, 4, 8, 17408, 5120, "mfma_stream_t16"),
+    (1, 4, 9, 17408, 5120, "mfma_reg_t32"), (1, 4, 32, 17408, 5120, "mfma_reg_t32"),
+    (1, 4, 33, 17408, 5120, "mfma_reg_t64"), (1, 4, 64, 17408, 5120, "mfma_reg_t64"),
+    (1, 5, 9, 8192, 5120, "mfma_reg_t16"), (1, 5, 17, 8192, 5120, "mfma_reg_t32"),
+    (1, 5, 48, 8192, 5120, "mfma_reg_t64"), (1, 5, 49, 8192, 5120, "mfma_bal_t64"),
+    # K > 5120: streaming to 4 tokens (the register ring from the first token beyond K = 8192),
+    # the register ring to 24, the narrow kernel beyond
+    (0, 5, 4, 5120, 6144, "mfma_stream_t16"), (0, 4, 4, 5120, 8192, "mfma_stream_t16"),
+    (0, 5, 1, 5120, 12288, "mfma_reg_t16"), (2, 4, 4, 5120, 17408, "mfma_reg_t16"),
+    (2, 5, 5, 5120, 6144, "mfma_reg_t16"), (0, 4, 16, 5120, 8192, "mfma_reg_t16"),
+    (0, 5, 17, 5120, 17408, "mfma_reg_t32"), (2, 5, 24, 5120, 6144, "mfma_reg_t32"),
+    (0, 4, 25, 5120, 8192, "mfma_narrow_t32"), (0, 5, 64, 5120, 12288, "mfma_narrow_t64"),
+    # the SwiGLU pair at K > 5120 (no measured shape): streaming to 16, narrow beyond
+    (1, 5, 16, 5120, 6144, "mfma_stream_t16"), (1, 5, 17, 5120, 6144, "mfma_narrow_t32"),
 ])
-def test_route_choice_follows_measured_crossovers(op, bits, T, K, route):
-    assert w4.route_name(w4.route_for(op, bits, T, 5120, K)) == route
+def test_route_choice_follows_measured_crossovers(op, bits, T, N, K, route):
+    assert w4.route_name(w4.route_for(op, bits, T, N, K)) == route
 
 
 def test_route_for_rejects_bad_shapes():

@@ -18,9 +18,11 @@ from gpu_util import assert_close, canon, to_np
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 N = 784
-# route -> widths: 4-row slice, 8-row slice, 16-row slice, 32-row ring, 64-row ring
+# route -> widths: 4-row slice, 8-row slice, 16-row slice, 32-row ring, 64-row ring, the
+# balanced narrow kernel and the register ring
 CASES = [("mfma_stream_t16", t) for t in (4, 5, 8, 9, 16)] + [("mfma_stream_t32", t) for t in (17, 32)] + \
-        [("mfma_stream_t64", t) for t in (33, 64)] + [("mfma_bal_t32", 24), ("mfma_bal_t64", 64)]
+        [("mfma_stream_t64", t) for t in (33, 64)] + [("mfma_bal_t32", 24), ("mfma_bal_t64", 64)] + \
+        [("mfma_reg_t16", 4), ("mfma_reg_t16", 16), ("mfma_reg_t32", 32), ("mfma_reg_t64", 64)]
 
 
 @pytest.mark.parametrize("K", [5120, 5056])

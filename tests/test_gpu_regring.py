@@ -1,0 +1,108 @@
+"""GPU tier: the register-ring kernel (routes mfma_reg_t16 / _t32 / _t64).
+
+Each workgroup takes an even share of the row tiles (one workgroup per compute unit, up to six
+16-row tiles, or five gate / up tile pairs for the SwiGLU op); the row counts below give every
+instance size, shares that differ by one unit (the last unit of a share is then absent), and
+grids of more than one round.  K covers waves without any k-block (K = 320: three blocks for
+four waves), a half-size last block, ring loops with a remainder, and long rows.  Every output
+is compared with the fp64 oracle.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import w4_groupwise_gemm_amd as w4
+from synth import make_weights, make_activations, make_residual
+from gpu_util import assert_close, canon, to_np
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+# units (16-row tiles, or tile pairs for SwiGLU) -> largest share with 256 workgroups:
+# 100 -> 1, 300 -> 2, 600 -> 3, 900 -> 4, 1200 -> 5, 1500 -> 6 (linear cap), 1700 -> 6 in
+# 284 workgroups; SwiGLU: 1400 -> 5 pairs in 280 workgroups
+LINEAR_UNITS = [100, 300, 600, 900, 1200, 1500, 1700]
+SWIGLU_UNITS = [100, 300, 600, 900, 1200, 1400]
+ROUTE_T = [("mfma_reg_t16", 1), ("mfma_reg_t16", 16), ("mfma_reg_t32", 17), ("mfma_reg_t32", 32),
+           ("mfma_reg_t64", 33), ("mfma_reg_t64", 64)]
+
+
+def route_id(name):
+    return {w4.route_name(i): i for i in range(w4.route_count())}[name]
+
+
+def _run(route, op, N, K, T, bits, seed, zero=("uniform", 6, 9)):
+    rng = np.random.default_rng(seed)
+    scale = (0.0025, 0.01) if bits == 5 else (0.005, 0.02)
+    ws = [make_weights(rng, "w", N, K, bits, zero, scale)]
+    if op == w4.OP_SWIGLU:
+        ws.append(make_weights(rng, "u", N, K, bits, zero, scale))
+    x, _ = make_activations(rng, T, K, 0.5 if op == w4.OP_SWIGLU else 1.0, 0)
+    r = make_residual(rng, T, N) if op == w4.OP_ADD else None
+    if op == w4.OP_SWIGLU:
+        pw = w4.pack_pair(canon(ws[0]), canon(ws[1]), bits, device=DEV)
+        ref = oracle.swiglu(x, canon(ws[0]), canon(ws[1]), bits=bits)
+    elif op == w4.OP_ADD:
+        pw = w4.pack_weight(*canon(ws[0]), bits, device=DEV)
+        ref = oracle.linear_add(x, *canon(ws[0]), r, bits=bits)
+    else:
+        pw = w4.pack_weight(*canon(ws[0]), bits, device=DEV)
+        ref = oracle.linear(x, *canon(ws[0]), bits=bits)
+    print(f"case route={route} op={op} bits={bits} T={T} N={N} K={K}", flush=True)
+    rd = torch.from_numpy(r).to(DEV) if r is not None else None
+    y = w4.linear_route(route_id(route), op, torch.from_numpy(x).to(DEV), pw, residual=rd)
+    torch.cuda.synchronize()
+    # the SwiGLU pair is held to the relative L2 bound only beyond K = 5120: its largest element
+    # error grows with K (the fp16-weight arithmetic alone exceeds the element bound there:
+    # tests/test_weight_rounding_model.py)
+    assert_close(to_np(y), ref, f"{route} op{op} b{bits} T{T} N{N} K{K}",
+                 elem=not (op == w4.OP_SWIGLU and K > 5120))
+
+
+@pytest.mark.parametrize("bits", [4, 5])
+@pytest.mark.parametrize("units", LINEAR_UNITS)
+@pytest.mark.parametrize("route,T", ROUTE_T)
+def test_regring_linear_shares(route, T, units, bits):
+    _run(route, w4.OP_LINEAR, 16 * units, 320, T, bits, seed=units + T + bits)
+
+
+@pytest.mark.parametrize("bits", [4, 5])
+@pytest.mark.parametrize("units", SWIGLU_UNITS)
+@pytest.mark.parametrize("route,T", ROUTE_T)
+def test_regring_swiglu_shares(route, T, units, bits):
+    _run(route, w4.OP_SWIGLU, 16 * units, 320, T, bits, seed=3 * units + T + bits)
+
+
+# K = 1088: a half-size last block; 2112: 17 blocks over four waves (5, 4, 4, 4: ring loops
+# with a remainder); 6208: 48 blocks and a half; 17408: 136 blocks
+@pytest.mark.parametrize("bits", [4, 5])
+@pytest.mark.parametrize("K", [1088, 2112, 6208, 17408])
+@pytest.mark.parametrize("route,T", [("mfma_reg_t16", 7), ("mfma_reg_t32", 20), ("mfma_reg_t64", 64)])
+@pytest.mark.parametrize("op", [w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD])
+def test_regring_k_lengths(op, route, T, K, bits):
+    _run(route, op, 16 * 40, K, T, bits, seed=K + T + op + bits)
+
+
+@pytest.mark.parametrize("route,T", [("mfma_reg_t16", 5), ("mfma_reg_t64", 40)])
+def test_regring_fractional_zero_points(route, T):
+    # zero-points with a fraction take the exact split into integer and fractional parts
+    _run(route, w4.OP_LINEAR, 16 * 300, 1088, T, 4, seed=T, zero=("real", 3.0, 12.0))
+
+
+@pytest.mark.parametrize("route", ["mfma_reg_t16", "mfma_reg_t32", "mfma_reg_t64"])
+def test_regring_deterministic(route):
+    N, K, T, bits = 16 * 900, 2048, 16, 4
+    rng = np.random.default_rng(11)
+    ws = make_weights(rng, "w", N, K, bits, ("uniform", 6, 9), (0.005, 0.02))
+    x, _ = make_activations(rng, T, K, 1.0, 0)
+    pw = w4.pack_weight(*canon(ws), bits, device=DEV)
+    xd = torch.from_numpy(x).to(DEV)
+    rid = route_id(route)
+    first = to_np(w4.linear_route(rid, w4.OP_LINEAR, xd, pw)).view(np.uint16)
+    for _ in range(4):
+        again = to_np(w4.linear_route(rid, w4.OP_LINEAR, xd, pw)).view(np.uint16)
+        assert np.array_equal(first, again)

@@ -34,6 +34,9 @@ ROUTE_TS = {
     "mfma_stream_t64": (33, 64),
     "mfma_bal_t32": (5, 32),
     "mfma_bal_t64": (33, 64),
+    "mfma_reg_t16": (1, 16),
+    "mfma_reg_t32": (5, 32),
+    "mfma_reg_t64": (33, 64),
 }
 
 

@@ -23,7 +23,8 @@ PROBE_LIB = os.path.join(HERE, "libw4probe.so")  # measurement support (read/cop
 STREAM_PARTS = [("stream.hip", [f"-DW4_STREAM_BITS={b}", f"-DW4_STREAM_EPI={e}"], f"stream_b{b}_e{e}.o")
                 for b in (4, 5) for e in (0, 1, 2)]
 NARROW_PARTS = [("narrow.hip", [f"-DW4_NARROW_BITS={b}"], f"narrow_b{b}.o") for b in (4, 5)]
-SOURCES = STREAM_PARTS + NARROW_PARTS + ["api.hip", "splitk.hip", "wide.hip", "bf16.hip", "a8.hip", "repack.cpp", "graphs.cpp"]
+REGRING_PARTS = [("regring.hip", [f"-DW4_REGRING_BITS={b}"], f"regring_b{b}.o") for b in (4, 5)]
+SOURCES = STREAM_PARTS + NARROW_PARTS + REGRING_PARTS + ["api.hip", "splitk.hip", "wide.hip", "bf16.hip", "a8.hip", "repack.cpp", "graphs.cpp"]
 PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else "hipcc")

@@ -29,7 +29,8 @@ enum RouteKind {
   KIND_SPLITK = 4,
   KIND_STREAM32 = 5,
   KIND_STREAM64 = 6,
-  KIND_BALANCED = 7
+  KIND_BALANCED = 7,
+  KIND_REGRING = 8
 };
 
 struct Route {
@@ -51,11 +52,14 @@ const Route kRoutes[] = {
     {"mfma_stream_t64", 1, 64, KIND_STREAM64, 64},
     {"mfma_bal_t32", 1, 32, KIND_BALANCED, 32},
     {"mfma_bal_t64", 1, 64, KIND_BALANCED, 64},
+    {"mfma_reg_t16", 1, 16, KIND_REGRING, 16},
+    {"mfma_reg_t32", 1, 32, KIND_REGRING, 32},
+    {"mfma_reg_t64", 1, 64, KIND_REGRING, 64},
 };
 constexpr int kNumRoutes = sizeof(kRoutes) / sizeof(kRoutes[0]);
 // route ids (indices into kRoutes; R_N16 is the 16-token streaming route)
 enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5, R_NTILED = 6, R_S32 = 7,
-       R_S64 = 8, R_B32 = 9, R_B64 = 10 };
+       R_S64 = 8, R_B32 = 9, R_B64 = 10, R_R16 = 11, R_R32 = 12, R_R64 = 13 };
 
 constexpr int kMaxDim = 1 << 24;
 
@@ -128,52 +132,69 @@ int device_check() {
 }
 
 // Boundaries from route sweeps on this chip (every route timed at the same T, cold weights, at
-// the decode, batched-decode, SwiGLU-pair and 5120-row prefill shapes); the reasons are given
-// case by case below.
+// the decode, batched-decode, SwiGLU-pair and 5120-row prefill shapes and at 5120-row matrices
+// of K = 8192 .. 17408); the reasons are given case by case below.
 int pick_route(int op, int bits, int T, int N, int K) {
-  // Crossovers measured per route on cold weights (5120 output rows unless named; us):
-  //  * K <= 5120: the streaming route holds each wave's activation slice in LDS, which keeps it
-  //    ahead up to its 16-token limit (4-bit, T = 16: 10.7 against 14.7 with split K; 5-bit
-  //    13.1 against 23.3); for 17-32 tokens its 32-row ring leads (T = 32: 13.2 against 15.8
-  //    for the narrow kernel, 5-bit 15.1 against 18.0; SwiGLU pair 44.4 against 45.7).
-  //  * K > 5120: beyond 4 tokens the streaming route's activation fragments ride in its load
-  //    ring and split K leads (8192 / 12288 / 17408 columns at T = 16, 5-bit: 16.8 / 23.3 /
-  //    31.4 against 21.2 / 30.5 / 43.6 streamed and 17.4 / 23.8 / 32.3 narrow) to 20 tokens
-  //    with 4-bit codes and to 17 with 5-bit codes (14 at 6144 columns), after which the
-  //    narrow kernel leads (boundaries below).  The SwiGLU pair streams two row tiles per
-  //    workgroup, which keeps the streaming route ahead up to 16 tokens, and the narrow kernel
-  //    after that (split K: 41.7 against 32.1 streamed at T = 16, 44.0 against 42.9 narrow at 20).
-  //  * 33-64 tokens: the streaming kernel's one-slot 64-row ring is ahead for single 4-bit
-  //    matrices at K <= 5120 (T = 64: 17.7 against 20.5); the narrow kernel is ahead for 5-bit
-  //    codes (22.7 against 26.8) and at longer K (8192 x 5-bit: 23.3 against 23.6).
-  //  * The SwiGLU pair at K <= 5120 (17408 x 2 rows): the narrow kernel with its rows spread
-  //    evenly over one workgroup per compute unit (4-5 pairs each) leads from 12 tokens (T = 12
-  //    / 16 / 24 / 32 / 64: 31.1 / 31.5 / 31.4 / 31.7 / 51.7 us against 31.8 / 32.1 streamed,
-  //    40.5 / 42.3 with the 32-row ring, 58.7 narrow in pairs of two); the streaming route's
-  //    8-row slice keeps T <= 8 (24.8 against 31.2).  For single matrices of 5120 rows the
-  //    even spread (1-2 tiles per workgroup) trails the narrow kernel's pairs by 2-8 %.
+  // Crossovers measured per route on cold weights (us per launch):
+  //  * K <= 5120, single matrices: the streaming route holds each wave's activation slice in LDS
+  //    and leads to 16 tokens, its 32-row ring to 32 and its 64-row ring to 64 with 4-bit codes
+  //    (12288 x 5120, T = 16 / 32 / 64: 11.1 / 12.4 / 18.7 against 12.4 / 16.1 / 25.7 for the
+  //    register ring).  With 5-bit codes (more vector work per code byte) the register ring
+  //    leads at 5-16 tokens (12288 rows, T = 8: 11.7 against 13.2) and at 33-48 (T = 33 / 48:
+  //    19.0 / 22.3 against 21.5 / 22.5 narrow), the narrow kernel beyond.
+  //  * The SwiGLU pair at K <= 5120 depends on the pairs per compute unit.  One or fewer (4096
+  //    rows): the streaming routes throughout (T = 16 / 32 / 64: 8.7 / 10.1 / 14.7 against 10.3 /
+  //    14.9 / 24.2 register ring, 13.1 / 13.4 / 17.4 evenly spread narrow).  More: the streaming
+  //    route to 8 tokens (17408 rows, T = 8: 25.9 against 27.2), then the register ring, whose
+  //    32-token instance already leads at 9-16 tokens when a compute unit holds three or more
+  //    pairs (17408 rows, T = 16 / 32 / 64: 27.2 / 28.8 / 39.1 against 31.6 / 31.6 / 47.1 evenly
+  //    spread narrow); with two (5-bit 8192 rows) its 16-token instance to 16 (15.8 against
+  //    17.7 streamed), and the evenly spread narrow kernel above 48 (T = 64: 25.8 against 27.7).
+  //  * K > 5120, single matrices (5120 rows, K = 6144 .. 17408): the register ring leads from 5
+  //    tokens to 24, and from the first token once K > 8192 (5-bit 17408 columns, T = 1 / 8 /
+  //    16: 21.7 / 21.2 / 24.5 against 23.1 streamed, 26.4 / 31.2 split K; 4-bit 8192 columns,
+  //    T = 1: 10.8 against 9.3 streamed); split K no longer leads anywhere.  The narrow kernel
+  //    takes 25-64 tokens.
+  //  * The SwiGLU pair at K > 5120 has no measured shape (the pair's workloads all have
+  //    K = 5120); it keeps the order measured before the register ring existed.
   if (K <= 5120) {
     if (op == W4_OP_SWIGLU) {
-      if (T <= 8) return R_N16;
-      if (T <= 32) return R_B32;
-      if (T <= 64) return R_B64;
+      const int pairs = N / 16;
+      if (pairs <= 256) {
+        if (T <= 16) return R_N16;
+        if (T <= 32) return R_S32;
+        if (T <= 64) return R_S64;
+      } else {
+        if (T <= 8) return R_N16;
+        if (pairs >= 3 * 256) {
+          if (T <= 32) return R_R32;
+          if (T <= 64) return R_R64;
+        } else {
+          if (T <= 16) return R_R16;
+          if (T <= 32) return R_R32;
+          if (T <= 48) return R_R64;
+          if (T <= 64) return R_B64;
+        }
+      }
+    } else if (bits == 5) {
+      if (T <= 4) return R_N16;
+      if (T <= 16) return R_R16;
+      if (T <= 32) return R_S32;
+      if (T <= 48) return R_R64;
+      if (T <= 64) return R_N64;
     } else {
       if (T <= 16) return R_N16;
       if (T <= 32) return R_S32;
-      if (T <= 64) return bits == 5 ? R_N64 : R_S64;
+      if (T <= 64) return R_S64;
     }
   } else if (op == W4_OP_SWIGLU) {
     if (T <= 16) return R_N16;
     if (T <= 32) return R_N32;
     if (T <= 64) return R_N64;
   } else {
-    // split K to 20 tokens with 4-bit codes; with 5-bit codes (more vector work per weight byte)
-    // the narrow kernel catches up earlier, at 15 tokens for K = 6144 and 18 beyond (T = 16 at
-    // 6144 columns: 14.5 against 15.1 us; T = 17 / 20 at 8192: 17.2 / 18.2 split against 17.5 /
-    // 17.6; 4-bit 8192 at T = 20: 16.2 against 17.2, at 24: 17.7 against 17.3)
-    if (T <= 4) return R_N16;
-    const int split_max = bits == 4 ? 20 : K <= 6144 ? 14 : 17;
-    if (T <= split_max) return R_SPLITK;
+    if (T <= 4) return K > 8192 ? R_R16 : R_N16;
+    if (T <= 16) return R_R16;
+    if (T <= 24) return R_R32;
     if (T <= 32) return R_N32;
     if (T <= 64) return R_N64;
   }
@@ -217,6 +238,7 @@ int launch_route(int route, int op, const void* x, const void* w, const void* s,
     case KIND_STREAM: e = w4::launch_stream16(bits, epi, a, st); break;
     case KIND_NARROW: e = w4::launch_narrow(R.tn, false, bits, epi, a, st); break;
     case KIND_BALANCED: e = w4::launch_narrow(R.tn, true, bits, epi, a, st); break;
+    case KIND_REGRING: e = w4::launch_regring(R.tn, bits, epi, a, st); break;
     case KIND_WIDE: e = w4::launch_wide(bits, epi, a, st); break;
     case KIND_SPLITK: e = w4::launch_splitk(bits, epi, a, st); break;
     case KIND_STREAM32:

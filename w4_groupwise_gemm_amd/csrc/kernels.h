@@ -127,6 +127,13 @@ inline hipError_t launch_narrow(int tn, bool balanced, int bits, int epi, const 
   return bits == 5 ? launch_narrow_b5(tn, balanced, epi, a, stream)
                    : launch_narrow_b4(tn, balanced, epi, a, stream);
 }
+// register-ring kernel (regring.hip): T <= tn (16, 32 or 64) tokens, any K; row tiles spread
+// evenly over one workgroup per compute unit
+hipError_t launch_regring_b4(int tn, int epi, const KArgs& a, hipStream_t stream);
+hipError_t launch_regring_b5(int tn, int epi, const KArgs& a, hipStream_t stream);
+inline hipError_t launch_regring(int tn, int bits, int epi, const KArgs& a, hipStream_t stream) {
+  return bits == 5 ? launch_regring_b5(tn, epi, a, stream) : launch_regring_b4(tn, epi, a, stream);
+}
 // A8 route (a8.hip): int8 activations with a scale per 64 columns, and the int8 GEMM over them
 // (a.x holds the int8 codes; sx the scales, [ceil(K/128)][T][2])
 hipError_t launch_a8_quant(const _Float16* x, int T, int K, int8_t* xq, float* sx, hipStream_t stream);

@@ -76,6 +76,7 @@ KERNEL_SOURCES = {
     "stream_kernel": ["stream.hip", "device.h", "layout.h", "kernels.h", "api.hip"],
     "narrow_kernel": ["narrow.hip", "tile32.h", "device.h", "layout.h", "kernels.h", "api.hip"],
     "wide_kernel": ["wide.hip", "tile32.h", "device.h", "layout.h", "kernels.h", "api.hip"],
+    "regring_kernel": ["regring.hip", "tile32.h", "device.h", "layout.h", "kernels.h", "api.hip"],
 }
 
 

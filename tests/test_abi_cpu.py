@@ -72,13 +72,18 @@ def test_route_table_domains_cover_every_width():
     (1, 4, 33, 17408, 5120, "mfma_reg_t64"), (1, 4, 64, 17408, 5120, "mfma_reg_t64"),
     (1, 5, 9, 8192, 5120, "mfma_reg_t16"), (1, 5, 17, 8192, 5120, "mfma_reg_t32"),
     (1, 5, 48, 8192, 5120, "mfma_reg_t64"), (1, 5, 49, 8192, 5120, "mfma_bal_t64"),
-    # K > 5120: streaming to 4 tokens (the register ring from the first token beyond K = 8192),
-    # the register ring to 24, the narrow kernel beyond
+    # K > 5120: streaming to 4 tokens (the 16-row register ring from the first token beyond
+    # K = 8192), the 16-row register ring to 12 (16 below K = 12288), the 32-row ring beyond,
+    # and from the first token beyond K = 16384
     (0, 5, 4, 5120, 6144, "mfma_stream_t16"), (0, 4, 4, 5120, 8192, "mfma_stream_t16"),
-    (0, 5, 1, 5120, 12288, "mfma_reg_t16"), (2, 4, 4, 5120, 17408, "mfma_reg_t16"),
+    (0, 5, 1, 5120, 12288, "mfma_reg_t16"), (2, 4, 4, 5120, 17408, "mfma_reg32_t32"),
+    (0, 4, 1, 5120, 17408, "mfma_reg32_t32"), (0, 5, 16, 5120, 16384, "mfma_reg32_t32"),
+    (0, 5, 4, 5120, 16384, "mfma_reg_t16"),
     (2, 5, 5, 5120, 6144, "mfma_reg_t16"), (0, 4, 16, 5120, 8192, "mfma_reg_t16"),
-    (0, 5, 17, 5120, 17408, "mfma_reg_t32"), (2, 5, 24, 5120, 6144, "mfma_reg_t32"),
-    (0, 4, 25, 5120, 8192, "mfma_narrow_t32"), (0, 5, 64, 5120, 12288, "mfma_narrow_t64"),
+    (0, 5, 12, 5120, 12288, "mfma_reg_t16"), (0, 5, 13, 5120, 12288, "mfma_reg32_t32"),
+    (0, 5, 17, 5120, 17408, "mfma_reg32_t32"), (2, 5, 24, 5120, 6144, "mfma_reg32_t32"),
+    (0, 4, 32, 5120, 8192, "mfma_reg32_t32"), (0, 4, 33, 5120, 8192, "mfma_reg32_t64"),
+    (0, 5, 64, 5120, 12288, "mfma_reg32_t64"),
     # the SwiGLU pair at K > 5120 (no measured shape): streaming to 16, narrow beyond
     (1, 5, 16, 5120, 6144, "mfma_stream_t16"), (1, 5, 17, 5120, 6144, "mfma_narrow_t32"),
 ])

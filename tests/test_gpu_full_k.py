@@ -22,7 +22,8 @@ N = 784
 # balanced narrow kernel and the register ring
 CASES = [("mfma_stream_t16", t) for t in (4, 5, 8, 9, 16)] + [("mfma_stream_t32", t) for t in (17, 32)] + \
         [("mfma_stream_t64", t) for t in (33, 64)] + [("mfma_bal_t32", 24), ("mfma_bal_t64", 64)] + \
-        [("mfma_reg_t16", 4), ("mfma_reg_t16", 16), ("mfma_reg_t32", 32), ("mfma_reg_t64", 64)]
+        [("mfma_reg_t16", 4), ("mfma_reg_t16", 16), ("mfma_reg_t32", 32), ("mfma_reg_t64", 64),
+         ("mfma_reg32_t32", 16), ("mfma_reg32_t32", 32), ("mfma_reg32_t64", 64)]
 
 
 @pytest.mark.parametrize("K", [5120, 5056])

@@ -34,6 +34,8 @@ ROUTE_TS = {
     "mfma_reg_t16": (1, 2, 4, 5, 9, 16),
     "mfma_reg_t32": (1, 3, 17, 32),
     "mfma_reg_t64": (1, 17, 33, 40, 64),
+    "mfma_reg32_t32": (1, 5, 20, 32),
+    "mfma_reg32_t64": (1, 33, 64),
 }
 
 

@@ -1,4 +1,4 @@
-"""GPU tier: the register-ring kernel (routes mfma_reg_t16 / _t32 / _t64).
+"""GPU tier: the register-ring kernels (routes mfma_reg_t16 / _t32 / _t64, mfma_reg32_t32 / _t64).
 
 Each workgroup takes an even share of the row tiles (one workgroup per compute unit, up to six
 16-row tiles, or five gate / up tile pairs for the SwiGLU op); the row counts below give every
@@ -28,7 +28,8 @@ DEV = "cuda:0"
 LINEAR_UNITS = [100, 300, 600, 900, 1200, 1500, 1700]
 SWIGLU_UNITS = [100, 300, 600, 900, 1200, 1400]
 ROUTE_T = [("mfma_reg_t16", 1), ("mfma_reg_t16", 16), ("mfma_reg_t32", 17), ("mfma_reg_t32", 32),
-           ("mfma_reg_t64", 33), ("mfma_reg_t64", 64)]
+           ("mfma_reg_t64", 33), ("mfma_reg_t64", 64), ("mfma_reg32_t32", 1), ("mfma_reg32_t32", 20),
+           ("mfma_reg32_t32", 32), ("mfma_reg32_t64", 33), ("mfma_reg32_t64", 64)]
 
 
 def route_id(name):
@@ -81,10 +82,26 @@ def test_regring_swiglu_shares(route, T, units, bits):
 # with a remainder); 6208: 48 blocks and a half; 17408: 136 blocks
 @pytest.mark.parametrize("bits", [4, 5])
 @pytest.mark.parametrize("K", [1088, 2112, 6208, 17408])
-@pytest.mark.parametrize("route,T", [("mfma_reg_t16", 7), ("mfma_reg_t32", 20), ("mfma_reg_t64", 64)])
+@pytest.mark.parametrize("route,T", [("mfma_reg_t16", 7), ("mfma_reg_t32", 20), ("mfma_reg_t64", 64),
+                                     ("mfma_reg32_t32", 20), ("mfma_reg32_t32", 24), ("mfma_reg32_t64", 64)])
 @pytest.mark.parametrize("op", [w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD])
 def test_regring_k_lengths(op, route, T, K, bits):
     _run(route, op, 16 * 40, K, T, bits, seed=K + T + op + bits)
+
+
+# The 32-row form splits K over the workgroups of a pair group when K has at least 64 blocks
+# and the split shortens the largest share; the slice count follows from the shape: 5120 rows
+# at K = 8192 take three slices, 3200 rows two, 640 rows at K = 12352 four (with a half-size
+# last block), the 640-row SwiGLU pair (40 pairs) four.
+SPLIT_CASES = [(w4.OP_LINEAR, 5120, 8192), (w4.OP_ADD, 3200, 8192), (w4.OP_LINEAR, 640, 12352),
+               (w4.OP_SWIGLU, 640, 12352)]
+
+
+@pytest.mark.parametrize("bits", [4, 5])
+@pytest.mark.parametrize("route,T", [("mfma_reg32_t32", 1), ("mfma_reg32_t32", 32), ("mfma_reg32_t64", 64)])
+@pytest.mark.parametrize("op,N,K", SPLIT_CASES)
+def test_regring32_k_split(op, N, K, route, T, bits):
+    _run(route, op, N, K, T, bits, seed=N + K + T + bits + op)
 
 
 @pytest.mark.parametrize("route,T", [("mfma_reg_t16", 5), ("mfma_reg_t64", 40)])
@@ -93,9 +110,11 @@ def test_regring_fractional_zero_points(route, T):
     _run(route, w4.OP_LINEAR, 16 * 300, 1088, T, 4, seed=T, zero=("real", 3.0, 12.0))
 
 
-@pytest.mark.parametrize("route", ["mfma_reg_t16", "mfma_reg_t32", "mfma_reg_t64"])
-def test_regring_deterministic(route):
-    N, K, T, bits = 16 * 900, 2048, 16, 4
+@pytest.mark.parametrize("route,N,K", [("mfma_reg_t16", 16 * 900, 2048), ("mfma_reg_t32", 16 * 900, 2048),
+                                       ("mfma_reg_t64", 16 * 900, 2048), ("mfma_reg32_t32", 16 * 900, 2048),
+                                       ("mfma_reg32_t64", 640, 12352)])
+def test_regring_deterministic(route, N, K):
+    T, bits = 16, 4
     rng = np.random.default_rng(11)
     ws = make_weights(rng, "w", N, K, bits, ("uniform", 6, 9), (0.005, 0.02))
     x, _ = make_activations(rng, T, K, 1.0, 0)

@@ -37,6 +37,8 @@ ROUTE_TS = {
     "mfma_reg_t16": (1, 16),
     "mfma_reg_t32": (5, 32),
     "mfma_reg_t64": (33, 64),
+    "mfma_reg32_t32": (5, 32),
+    "mfma_reg32_t64": (33, 64),
 }
 
 

@@ -30,7 +30,8 @@ enum RouteKind {
   KIND_STREAM32 = 5,
   KIND_STREAM64 = 6,
   KIND_BALANCED = 7,
-  KIND_REGRING = 8
+  KIND_REGRING = 8,
+  KIND_REGRING32 = 9
 };
 
 struct Route {
@@ -55,11 +56,13 @@ const Route kRoutes[] = {
     {"mfma_reg_t16", 1, 16, KIND_REGRING, 16},
     {"mfma_reg_t32", 1, 32, KIND_REGRING, 32},
     {"mfma_reg_t64", 1, 64, KIND_REGRING, 64},
+    {"mfma_reg32_t32", 1, 32, KIND_REGRING32, 32},
+    {"mfma_reg32_t64", 1, 64, KIND_REGRING32, 64},
 };
 constexpr int kNumRoutes = sizeof(kRoutes) / sizeof(kRoutes[0]);
 // route ids (indices into kRoutes; R_N16 is the 16-token streaming route)
 enum { R_GEMV = 0, R_N16 = 1, R_N32 = 2, R_N64 = 3, R_WIDE = 4, R_SPLITK = 5, R_NTILED = 6, R_S32 = 7,
-       R_S64 = 8, R_B32 = 9, R_B64 = 10, R_R16 = 11, R_R32 = 12, R_R64 = 13 };
+       R_S64 = 8, R_B32 = 9, R_B64 = 10, R_R16 = 11, R_R32 = 12, R_R64 = 13, R_Q32 = 14, R_Q64 = 15 };
 
 constexpr int kMaxDim = 1 << 24;
 
@@ -150,11 +153,14 @@ int pick_route(int op, int bits, int T, int N, int K) {
   //    pairs (17408 rows, T = 16 / 32 / 64: 27.2 / 28.8 / 39.1 against 31.6 / 31.6 / 47.1 evenly
   //    spread narrow); with two (5-bit 8192 rows) its 16-token instance to 16 (15.8 against
   //    17.7 streamed), and the evenly spread narrow kernel above 48 (T = 64: 25.8 against 27.7).
-  //  * K > 5120, single matrices (5120 rows, K = 6144 .. 17408): the register ring leads from 5
-  //    tokens to 24, and from the first token once K > 8192 (5-bit 17408 columns, T = 1 / 8 /
-  //    16: 21.7 / 21.2 / 24.5 against 23.1 streamed, 26.4 / 31.2 split K; 4-bit 8192 columns,
-  //    T = 1: 10.8 against 9.3 streamed); split K no longer leads anywhere.  The narrow kernel
-  //    takes 25-64 tokens.
+  //  * K > 5120, single matrices (5120 rows, K = 6144 .. 17408): the 32-row register ring, with
+  //    K split three ways over the workgroups from K = 8192, leads from 17 tokens, from 13 once
+  //    K >= 12288 and from the first token once K > 16384 (4-bit 17408 columns, T = 1 / 16 / 32
+  //    / 64: 18.6 / 19.5 / 19.5 / 28.6 against 19.4 / 22.7 16-row ring, 31.9 / 43.0 narrow;
+  //    5-bit 6144 columns, unsplit, T = 24 / 64: 12.9 / 18.9 against 14.5 / 19.9 before it).
+  //    Below, the 16-row register ring from 5 tokens, and from the first token once K > 8192
+  //    (5-bit 12288 columns, T = 1: 16.8 against 17.4 32-row ring); streaming at 1-4 tokens up
+  //    to K = 8192 (4-bit 8192 columns, T = 1: 9.3 against 10.9).
   //  * The SwiGLU pair at K > 5120 has no measured shape (the pair's workloads all have
   //    K = 5120); it keeps the order measured before the register ring existed.
   if (K <= 5120) {
@@ -192,11 +198,12 @@ int pick_route(int op, int bits, int T, int N, int K) {
     if (T <= 32) return R_N32;
     if (T <= 64) return R_N64;
   } else {
+    if (K > 16384 && T <= 32) return R_Q32;
     if (T <= 4) return K > 8192 ? R_R16 : R_N16;
-    if (T <= 16) return R_R16;
-    if (T <= 24) return R_R32;
-    if (T <= 32) return R_N32;
-    if (T <= 64) return R_N64;
+    if (T <= 12) return R_R16;
+    if (T <= 16) return K >= 12288 ? R_Q32 : R_R16;
+    if (T <= 32) return R_Q32;
+    if (T <= 64) return R_Q64;
   }
   // Above 64 tokens the wide kernel's workgroups (about 128 rows x 128 tokens each) leave most
   // compute units idle until there are about 128 of them; below that the narrow kernel run as
@@ -205,6 +212,53 @@ int pick_route(int op, int bits, int T, int N, int K) {
   const long long rows = op == W4_OP_SWIGLU ? 2LL * N : (long long)N;
   if ((rows + 127) / 128 * ((T + 127) / 128) < 128) return R_NTILED;
   return R_WIDE;
+}
+
+// ---- Workspace of the K split over workgroups (32-row register ring): static device arrays, one
+// slot per stream (calls on one stream never overlap; calls on different streams get different
+// slots).  Each slot's counters start at zero and every launch leaves them at zero.  A stream
+// beyond the last slot runs the routes without the split.
+constexpr int kSplitSlots = 4;
+constexpr size_t kSplitBytes = (size_t)8 << 20;
+constexpr int kSplitGroups = 256;
+__device__ __align__(256) float split_part[kSplitSlots][kSplitBytes / 4];
+__device__ __align__(256) int split_cnt[kSplitSlots][kSplitGroups] = {};
+
+struct SplitSlots {
+  char* part = nullptr;
+  int* cnt = nullptr;
+  hipStream_t owner[kSplitSlots] = {};
+  bool used[kSplitSlots] = {};
+};
+SplitSlots g_split[64];
+std::mutex g_split_mu;
+
+w4::SplitWs split_ws_for(hipStream_t st) {
+  w4::SplitWs none{nullptr, nullptr, 0, 0};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return none;
+  std::lock_guard<std::mutex> lock(g_split_mu);
+  SplitSlots& d = g_split[dev];
+  if (!d.part) {
+    void* p = nullptr;
+    void* c = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(split_part)) != hipSuccess || !p) return none;
+    if (hipGetSymbolAddress(&c, HIP_SYMBOL(split_cnt)) != hipSuccess || !c) return none;
+    d.part = static_cast<char*>(p);
+    d.cnt = static_cast<int*>(c);
+  }
+  int slot = -1;
+  for (int i = 0; i < kSplitSlots && slot < 0; ++i)
+    if (d.used[i] && d.owner[i] == st) slot = i;
+  for (int i = 0; i < kSplitSlots && slot < 0; ++i)
+    if (!d.used[i]) {
+      d.used[i] = true;
+      d.owner[i] = st;
+      slot = i;
+    }
+  if (slot < 0) return none;
+  return w4::SplitWs{reinterpret_cast<float*>(d.part + slot * kSplitBytes), d.cnt + slot * kSplitGroups,
+                     kSplitBytes, kSplitGroups};
 }
 
 // xexp: nullptr for fp16 activations and outputs; for bf16 ones, x is the prepared fp16 copy and
@@ -239,6 +293,7 @@ int launch_route(int route, int op, const void* x, const void* w, const void* s,
     case KIND_NARROW: e = w4::launch_narrow(R.tn, false, bits, epi, a, st); break;
     case KIND_BALANCED: e = w4::launch_narrow(R.tn, true, bits, epi, a, st); break;
     case KIND_REGRING: e = w4::launch_regring(R.tn, bits, epi, a, st); break;
+    case KIND_REGRING32: e = w4::launch_regring32(R.tn, bits, epi, a, split_ws_for(st), st); break;
     case KIND_WIDE: e = w4::launch_wide(bits, epi, a, st); break;
     case KIND_SPLITK: e = w4::launch_splitk(bits, epi, a, st); break;
     case KIND_STREAM32:

@@ -134,6 +134,25 @@ hipError_t launch_regring_b5(int tn, int epi, const KArgs& a, hipStream_t stream
 inline hipError_t launch_regring(int tn, int bits, int epi, const KArgs& a, hipStream_t stream) {
   return bits == 5 ? launch_regring_b5(tn, epi, a, stream) : launch_regring_b4(tn, epi, a, stream);
 }
+
+// Workspace of a K split over workgroups: fp32 partial sums, and one arrival counter per pair
+// group, each zero between launches (the last workgroup of a group resets its counter).  Calls
+// that share one workspace must not overlap in time.  part == nullptr: no split.
+struct SplitWs {
+  float* part;
+  int* cnt;
+  size_t part_bytes;
+  int groups;
+};
+
+// 32-row register ring (regring.hip): 32x32x16 steps on tile pairs, T <= tn (32 or 64) tokens,
+// any K; pairs spread evenly over one workgroup per compute unit, K optionally split
+hipError_t launch_regring32_b4(int tn, int epi, const KArgs& a, const SplitWs& ws, hipStream_t stream);
+hipError_t launch_regring32_b5(int tn, int epi, const KArgs& a, const SplitWs& ws, hipStream_t stream);
+inline hipError_t launch_regring32(int tn, int bits, int epi, const KArgs& a, const SplitWs& ws,
+                                   hipStream_t stream) {
+  return bits == 5 ? launch_regring32_b5(tn, epi, a, ws, stream) : launch_regring32_b4(tn, epi, a, ws, stream);
+}
 // A8 route (a8.hip): int8 activations with a scale per 64 columns, and the int8 GEMM over them
 // (a.x holds the int8 codes; sx the scales, [ceil(K/128)][T][2])
 hipError_t launch_a8_quant(const _Float16* x, int T, int K, int8_t* xq, float* sx, hipStream_t stream);

@@ -77,6 +77,7 @@ KERNEL_SOURCES = {
     "narrow_kernel": ["narrow.hip", "tile32.h", "device.h", "layout.h", "kernels.h", "api.hip"],
     "wide_kernel": ["wide.hip", "tile32.h", "device.h", "layout.h", "kernels.h", "api.hip"],
     "regring_kernel": ["regring.hip", "tile32.h", "device.h", "layout.h", "kernels.h", "api.hip"],
+    "regring32_kernel": ["regring.hip", "tile32.h", "device.h", "layout.h", "kernels.h", "api.hip"],
 }
 
 

@@ -282,12 +282,13 @@ __global__ __launch_bounds__(kNW * 64) void regring_kernel(KArgs a, RegPart part
 // counter; the last of the S adds the slices in slice order (bitwise reproducible whatever the
 // arrival order), runs the epilogue and resets the counter.  No workgroup waits for another.
 //
-// Load order and waits.  The compiler places the waits for code registers, and it counts only
-// register loads, so a direct-to-LDS load issued after a code block makes its wait drain that
-// load as well.  Sub-step j therefore runs: the wait for code block j (forced here, before
-// anything else is issued), the refill of activation slot (j + 1) % 2, code block j + 2, then the
-// explicit wait for activation block j, and the math.  The only direct-to-LDS load behind code
-// block j when it is waited for is then activation block j, which the math needs anyway.
+// Load order and waits.  The compiler places the waits for code registers (counting the
+// direct-to-LDS loads issued after a code block, so such a wait leaves them in flight); the wait
+// for an activation block is explicit.  Sub-step j runs: the wait for code block j (forced here,
+// before anything else is issued: activation block j and code block j + 1 stay in flight), the
+// refill of activation slot (j + 1) % 2, code block j + 2, then the explicit wait for activation
+// block j (code block j + 1, activation block j + 1 and code block j + 2 may still be in flight),
+// and the math.
 
 // f(integral_constant<int, i>) for i = 0 .. N-1, unrolled whatever the body's size (a plain loop
 // over pairs stays rolled for four or five pairs and sends the register arrays to scratch memory).

@@ -125,3 +125,67 @@ def test_regring_deterministic(route, N, K):
     for _ in range(4):
         again = to_np(w4.linear_route(rid, w4.OP_LINEAR, xd, pw)).view(np.uint16)
         assert np.array_equal(first, again)
+
+
+# ---- the K split's workspace: static device slots, one per stream (four), so that split calls
+# on different streams never share partial sums; a stream without a slot runs unsplit.
+def _split_inputs(seed, N=640, K=12352, T=32, bits=4):
+    rng = np.random.default_rng(seed)
+    w = make_weights(rng, "w", N, K, bits, ("uniform", 6, 9), (0.005, 0.02))
+    x, _ = make_activations(rng, T, K, 1.0, 0)
+    ref = oracle.linear(x, *canon(w), bits=bits)
+    return torch.from_numpy(x).to(DEV), w4.pack_weight(*canon(w), bits, device=DEV), ref
+
+
+def test_regring32_split_on_overlapping_streams():
+    rid = route_id("mfma_reg32_t32")
+    cases = [_split_inputs(100 + i) for i in range(6)]
+    streams = [torch.cuda.Stream() for _ in range(6)]
+    torch.cuda.synchronize()
+    outs = [[] for _ in range(6)]
+    print("case split on 6 streams, 3 rounds", flush=True)
+    for _ in range(3):
+        for i, (s, (x, pw, _)) in enumerate(zip(streams, cases)):
+            with torch.cuda.stream(s):
+                outs[i].append(w4.linear_route(rid, w4.OP_LINEAR, x, pw))
+    torch.cuda.synchronize()
+    for i, (_, _, ref) in enumerate(cases):
+        for y in outs[i]:
+            assert_close(to_np(y), ref, f"stream {i}")
+        assert all(torch.equal(y.view(torch.int16), outs[i][0].view(torch.int16)) for y in outs[i])
+
+
+@pytest.mark.parametrize("op", [w4.OP_LINEAR, w4.OP_SWIGLU])
+def test_regring32_split_graph_replays(op):
+    N, K, T, bits = 640, 12352, 24, 5
+    rng = np.random.default_rng(7 + op)
+    ws = [make_weights(rng, "w", N, K, bits, ("const", 16), (0.0025, 0.01))]
+    xn = make_activations(rng, T, K, 0.5 if op == w4.OP_SWIGLU else 1.0, 0)[0]
+    if op == w4.OP_SWIGLU:
+        ws.append(make_weights(rng, "u", N, K, bits, ("const", 16), (0.0025, 0.01)))
+        pw = w4.pack_pair(canon(ws[0]), canon(ws[1]), bits, device=DEV)
+        ref = oracle.swiglu(xn, canon(ws[0]), canon(ws[1]), bits=bits)
+    else:
+        pw = w4.pack_weight(*canon(ws[0]), bits, device=DEV)
+        ref = oracle.linear(xn, *canon(ws[0]), bits=bits)
+    x = torch.from_numpy(xn).to(DEV)
+    rid = route_id("mfma_reg32_t32")
+    print(f"case split graph op={op}", flush=True)
+    eager = w4.linear_route(rid, op, x, pw)
+    torch.cuda.synchronize()
+    static_out = torch.empty((T, N), dtype=torch.float16, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w4.linear_route(rid, op, x, pw, out=static_out)
+    first = None
+    for rep in range(4):
+        static_out.fill_(float("nan"))
+        again = w4.linear_route(rid, op, x, pw)  # eager split calls of the program between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(again.view(torch.int16), eager.view(torch.int16))
+        assert_close(to_np(static_out), ref, f"replay {rep}", elem=op != w4.OP_SWIGLU)
+        if first is None:
+            first = static_out.clone()
+        assert torch.equal(static_out.view(torch.int16), first.view(torch.int16))

@@ -30,6 +30,9 @@
 //    one 16x16x32 matrix-core step per 16-token tile;
 //  * the four partial sums are combined in LDS in a fixed order (bitwise deterministic), then the
 //    store / SwiGLU / add epilogue.
+// Its 32-row form (regring32_kernel, further below) runs 32x32x16 steps on tile pairs with the
+// activation blocks in a per-wave LDS ring instead of registers, and where pairs are few and K
+// long splits K over the workgroups of a pair group, the last of them adding the partial sums.
 #include "device.h"
 #include "kernels.h"
 #include "tile32.h"

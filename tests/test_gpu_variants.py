@@ -168,3 +168,39 @@ def test_bf16_public_calls_match_their_route():
             rid = w4.route_for(op, 4, T, N, K)
             y2 = w4.linear_route_bf16(rid, op, xd, pw, residual=rd if op == w4.OP_ADD else None)
             assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), (op, T)
+
+
+# The 32-row register ring with K split over workgroups (640 rows: 20 tile pairs, four K
+# slices): groups of 32 and 128 columns, and bf16 activations, residuals and outputs through the
+# split's last-workgroup epilogue.
+@pytest.mark.parametrize("route,T", [("mfma_reg32_t32", 24), ("mfma_reg32_t64", 64)])
+@pytest.mark.parametrize("group,K", [(32, 12352), (128, 16384)])
+def test_k_split_group_sizes(route, T, group, K):
+    N, bits = 640, 5
+    rng = np.random.default_rng(K + T + group)
+    ws, pw = _weights(rng, N, K, bits, w4.OP_ADD, group)
+    x, _ = make_activations(rng, T, K, 1.0, 4)
+    r = make_residual(rng, T, N)
+    print(f"case split group={group} route={route} T={T} K={K}", flush=True)
+    y = w4.linear_route(route_ids()[route], w4.OP_ADD, torch.from_numpy(x).to(DEV), pw,
+                        residual=torch.from_numpy(r).to(DEV))
+    torch.cuda.synchronize()
+    ref = _oracle(ws, x.astype(np.float64), r.astype(np.float64), w4.OP_ADD, bits, group)
+    assert_close(to_np(y), ref, f"split group {group} {route} T{T} K{K}")
+
+
+@pytest.mark.parametrize("op", [w4.OP_LINEAR, w4.OP_SWIGLU, w4.OP_ADD])
+def test_k_split_bf16(op):
+    N, K, bits, T = 640, 12352, 4, 32
+    rng = np.random.default_rng(300 + op)
+    ws, pw = _weights(rng, N, K, bits, op, 64)
+    xb, _ = make_activations_bf16(rng, T, K, 0.5 if op == w4.OP_SWIGLU else 1.0, 0)
+    rb = bf16_bits(rng.standard_normal((T, N)).astype(np.float32))
+    print(f"case split bf16 op={op}", flush=True)
+    y = w4.linear_route_bf16(route_ids()["mfma_reg32_t32"], op, _bf16_dev(xb), pw,
+                             residual=_bf16_dev(rb) if op == w4.OP_ADD else None)
+    torch.cuda.synchronize()
+    got = oracle.bf16_value(_bf16_np(y))
+    ref = _oracle(ws, oracle.bf16_value(xb), oracle.bf16_value(rb), op, bits, 64)
+    # (the SwiGLU pair beyond K = 5120 is held to the relative L2 bound)
+    assert_close(got, ref, f"split bf16 op{op}", elem=op != w4.OP_SWIGLU)

@@ -189,3 +189,14 @@ def test_regring32_split_graph_replays(op):
         if first is None:
             first = static_out.clone()
         assert torch.equal(static_out.view(torch.int16), first.view(torch.int16))
+
+
+# An odd number of 16-row tiles leaves the 32-row form's last pair without its second tile (its
+# lanes re-read the first tile, whose rows there are never stored): unsplit (K = 2112) and with
+# the K split (K = 12352, 41 tiles: 21 pairs in four slices).
+@pytest.mark.parametrize("bits", [4, 5])
+@pytest.mark.parametrize("op", [w4.OP_LINEAR, w4.OP_ADD])
+@pytest.mark.parametrize("route,T", [("mfma_reg32_t32", 9), ("mfma_reg32_t64", 40)])
+@pytest.mark.parametrize("tiles,K", [(301, 2112), (41, 12352), (1, 640)])
+def test_regring32_odd_tile_count(tiles, K, route, T, op, bits):
+    _run(route, op, 16 * tiles, K, T, bits, seed=tiles + K + T + op + bits)
